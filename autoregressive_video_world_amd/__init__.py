@@ -1,0 +1,8 @@
+"""Streaming block-causal chunk attention over a bounded KV ring, MI355X-native.
+
+The compute lives in ``libwm.so`` (C ABI declared in ``include/wm.h``, HIP
+kernels for gfx950 under ``csrc/``); ``binding`` marshals PyTorch tensors and
+streams into it.
+"""
+
+from .binding import KVRing, WMError, lib, EXPORTS  # noqa: F401

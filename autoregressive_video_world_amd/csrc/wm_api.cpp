@@ -1,0 +1,588 @@
+// Host runtime and C ABI of the streaming KV-ring attention library.
+//
+// The ring state of a rollout is two integers (frames committed since the
+// last reset, temporal origin t0); slots, positions and evictions follow in
+// closed form, so no call ever reads device memory back.  Cache reading:
+// S sink frames (the first S frames of a sequence, never evicted) plus a
+// FIFO window of W frames in S + W fixed slots -- FlashDreams blog post,
+// "Bounded Memory for Infinite Rollouts"; Cosmos3-H-Dreams model card,
+// "Software Integration" (static-shape KV cache).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "wm.h"
+#include "wm_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+wm_status fail(wm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+wm_status ok() {
+  g_err.clear();
+  return WM_OK;
+}
+
+std::mutex g_mu;
+std::set<const void*> g_live;
+
+bool sync_check_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("WM_SYNC_CHECK");
+    return e && atoi(e) != 0;
+  }();
+  return on;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// libm through volatile pointers: keeps the compiler from fusing cos/sin
+// into sincos or vectorising them, so every entry is the scalar libm result.
+double (*volatile g_cos)(double) = ::cos;
+double (*volatile g_sin)(double) = ::sin;
+double (*volatile g_pow)(double, double) = ::pow;
+
+struct Bands {
+  int dt, dh, dw;
+};
+
+bool bands_of(const wm_kvring_desc& d, Bands* b) {
+  if (d.rope_dims[0] || d.rope_dims[1] || d.rope_dims[2]) {
+    b->dt = d.rope_dims[0];
+    b->dh = d.rope_dims[1];
+    b->dw = d.rope_dims[2];
+  } else {
+    b->dh = b->dw = 2 * (d.head_dim / 6);
+    b->dt = d.head_dim - b->dh - b->dw;
+  }
+  if (b->dt < 0 || b->dh < 0 || b->dw < 0) return false;
+  if ((b->dt | b->dh | b->dw) & 1) return false;
+  if (b->dt + b->dh + b->dw != d.head_dim) return false;
+  if (b->dt / 2 > wm::kMaxTPairs) return false;
+  return true;
+}
+
+struct Layout {
+  size_t k_off, v_off, tab_off;
+  size_t hcos, hsin, wcos, wsin;  // byte offsets of the tables
+  size_t tab_bytes, total;
+};
+
+wm_status check_desc(const wm_kvring_desc* d, Bands* bands) {
+  if (!d) return fail(WM_E_ARG, "descriptor is NULL");
+  if (d->batch < 1 || d->batch > WM_MAX_BATCH)
+    return fail(WM_E_SHAPE, "batch %d not in [1, %d]", d->batch, WM_MAX_BATCH);
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads)
+    return fail(WM_E_SHAPE, "heads: Hq=%d must be a positive multiple of Hkv=%d", d->n_q_heads,
+                d->n_kv_heads);
+  if (d->n_q_heads > 256) return fail(WM_E_SHAPE, "Hq=%d above 256", d->n_q_heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(WM_E_SHAPE, "head_dim %d: only 64 and 128 are built", d->head_dim);
+  if (d->frame_h < 1 || d->frame_w < 1 || (int64_t)d->frame_h * d->frame_w > (1 << 20))
+    return fail(WM_E_SHAPE, "frame grid %dx%d out of range", d->frame_h, d->frame_w);
+  if (d->n_sink < 0 || d->window < 0 || d->n_sink + d->window > WM_MAX_RING)
+    return fail(WM_E_SHAPE, "sink %d + window %d must be in [0, %d]", d->n_sink, d->window,
+                WM_MAX_RING);
+  if (d->max_chunk < 1 || d->max_chunk > WM_MAX_CHUNK)
+    return fail(WM_E_SHAPE, "max_chunk %d not in [1, %d]", d->max_chunk, WM_MAX_CHUNK);
+  if (!(d->rope_theta > 1.0) || !isfinite(d->rope_theta))
+    return fail(WM_E_SHAPE, "rope_theta must be finite and > 1");
+  if (!bands_of(*d, bands))
+    return fail(WM_E_SHAPE, "rope_dims {%d,%d,%d}: bands must be even, sum to d, d_t <= %d",
+                d->rope_dims[0], d->rope_dims[1], d->rope_dims[2], 2 * wm::kMaxTPairs);
+  const int64_t nq = (int64_t)d->max_chunk * d->frame_h * d->frame_w;
+  if ((int64_t)(d->n_sink + d->window + d->max_chunk) * d->frame_h * d->frame_w >= ((int64_t)1 << 24))
+    return fail(WM_E_SHAPE, "visible keys (S+W+C)*Ft must stay below 2^24");
+  if (nq * d->n_q_heads * d->head_dim > (int64_t)1 << 31)
+    return fail(WM_E_SHAPE, "chunk tensor above 2^31 elements per rollout");
+  return WM_OK;
+}
+
+Layout layout_of(const wm_kvring_desc& d, const Bands& b) {
+  Layout L;
+  const size_t ft = (size_t)d.frame_h * d.frame_w;
+  const size_t half =
+      (size_t)d.batch * (d.n_sink + d.window) * d.n_kv_heads * ft * d.head_dim * sizeof(uint16_t);
+  L.k_off = 0;
+  L.v_off = align_up(half, 256);
+  L.tab_off = align_up(L.v_off + half, 256);
+  const size_t hb = (size_t)d.frame_h * (b.dh / 2) * sizeof(float);
+  const size_t wb = (size_t)d.frame_w * (b.dw / 2) * sizeof(float);
+  L.hcos = L.tab_off;
+  L.hsin = L.hcos + align_up(hb, 16);
+  L.wcos = L.hsin + align_up(hb, 16);
+  L.wsin = L.wcos + align_up(wb, 16);
+  L.tab_bytes = (L.wsin + align_up(wb, 16)) - L.tab_off;
+  L.total = align_up(L.tab_off + L.tab_bytes, 256);
+  return L;
+}
+
+// Inverse frequency of pair j in a band of width da: theta^(-(2j)/da), fp64.
+double inv_freq(double theta, int j, int da) { return g_pow(theta, -(2.0 * j) / (double)da); }
+
+}  // namespace
+
+struct wm_kvring {
+  wm_kvring_desc desc;
+  Bands bands;
+  Layout L;
+  int ft, R;
+  bool meta_only;
+  uint8_t* pool;
+  std::vector<int64_t> n_committed, t0;
+  std::vector<double> inv_t;
+};
+
+namespace {
+
+wm_status check_ring(const wm_kvring* r) {
+  if (!r) return fail(WM_E_ARG, "ring handle is NULL");
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_live.count(r)) return fail(WM_E_STATE, "ring handle is not live (destroyed?)");
+  return WM_OK;
+}
+
+wm_status check_dev(const void* p, const char* name) {
+  if (!p) return fail(WM_E_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(WM_E_ARG, "%s is not 16-byte aligned", name);
+  return WM_OK;
+}
+
+bool is_active(const uint8_t* active, int b) { return !active || active[b] != 0; }
+
+int64_t next_t(const wm_kvring* r, int b) { return r->t0[b] + r->n_committed[b]; }
+
+void t_row(const wm_kvring* r, int64_t t, float* c, float* s) {
+  const int np = r->bands.dt / 2;
+  for (int j = 0; j < np; ++j) {
+    const double ang = (double)t * r->inv_t[j];
+    c[j] = (float)g_cos(ang);
+    s[j] = (float)g_sin(ang);
+  }
+}
+
+void fill_tables_ptrs(const wm_kvring* r, wm::RopeParams* p) {
+  p->hcos = reinterpret_cast<const float*>(r->pool + r->L.hcos);
+  p->hsin = reinterpret_cast<const float*>(r->pool + r->L.hsin);
+  p->wcos = reinterpret_cast<const float*>(r->pool + r->L.wcos);
+  p->wsin = reinterpret_cast<const float*>(r->pool + r->L.wsin);
+  p->ft = r->ft;
+  p->fw = r->desc.frame_w;
+  p->d = r->desc.head_dim;
+  p->dt2 = r->bands.dt / 2;
+  p->dh2 = r->bands.dh / 2;
+  p->dw2 = r->bands.dw / 2;
+  p->ring_slots = r->R;
+}
+
+wm_status hip_fail(hipError_t e, const char* what) {
+  return fail(WM_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+wm_status finish(hipStream_t s) {
+  if (sync_check_enabled()) {
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "asynchronous error");
+  }
+  return ok();
+}
+
+// --- the unchecked workers (arguments validated by the callers) -----------
+
+wm_status do_rope(const wm_kvring* r, const wm_bf16* x, wm_bf16* y, int n_heads, int n_frames,
+                  const int64_t* t_first, const uint8_t* active, hipStream_t s) {
+  wm::RopeParams p;
+  memset(&p, 0, sizeof p);
+  fill_tables_ptrs(r, &p);
+  p.x = x;
+  p.y = y;
+  p.n_heads = n_heads;
+  p.x_b_stride = (int64_t)n_frames * r->ft * n_heads * r->desc.head_dim;
+  for (int b = 0; b < r->desc.batch; ++b) {
+    if (!is_active(active, b)) continue;
+    const int64_t t0 = t_first ? t_first[b] : next_t(r, b);
+    for (int j = 0; j < n_frames; ++j) {
+      wm::RopeRow& row = p.rows[p.n_rows];
+      row.b = b;
+      row.j = j;
+      row.slot = -1;
+      t_row(r, t0 + j, p.tcos[p.n_rows], p.tsin[p.n_rows]);
+      if (++p.n_rows == wm::kRopeRows) {
+        hipError_t e = wm::launch_rope3d(p, s);
+        if (e != hipSuccess) return hip_fail(e, "rope3d launch");
+        p.n_rows = 0;
+      }
+    }
+  }
+  if (p.n_rows) {
+    hipError_t e = wm::launch_rope3d(p, s);
+    if (e != hipSuccess) return hip_fail(e, "rope3d launch");
+  }
+  return WM_OK;
+}
+
+// Closed-form plan of one append for rollout b (see the pool layout in wm.h).
+struct Planned {
+  int32_t slot;
+  bool stored;
+};
+
+void plan_append(const wm_kvring* r, int b, int n_frames, wm_append_report* rep,
+                 Planned* plan) {
+  const int64_t S = r->desc.n_sink, W = r->desc.window;
+  const int64_t m0 = r->n_committed[b], m_end = m0 + n_frames;
+  rep->n_written = n_frames;
+  rep->n_evicted = 0;
+  for (int j = 0; j < n_frames; ++j) {
+    const int64_t f = m0 + j;
+    int32_t slot;
+    if (f < S)
+      slot = (int32_t)f;
+    else if (W > 0)
+      slot = (int32_t)(S + (f - S) % W);
+    else
+      slot = -1;
+    rep->frame[j] = f;
+    rep->slot[j] = slot;
+    rep->t[j] = r->t0[b] + f;
+    if (W > 0 && f >= S + W) rep->evicted[rep->n_evicted++] = f - W;
+    plan[j].slot = slot;
+    plan[j].stored = slot >= 0 && (f < S || f >= m_end - W);
+  }
+}
+
+wm_status do_append(wm_kvring* r, const wm_bf16* k_raw, const wm_bf16* v, int n_frames,
+                    const uint8_t* active, wm_append_report* rep, hipStream_t s) {
+  const int B = r->desc.batch;
+  std::vector<wm_append_report> reps(B);
+  std::vector<Planned> plan((size_t)B * n_frames);
+  for (int b = 0; b < B; ++b) {
+    memset(&reps[b], 0, sizeof(wm_append_report));
+    if (is_active(active, b)) plan_append(r, b, n_frames, &reps[b], &plan[(size_t)b * n_frames]);
+  }
+  if (!r->meta_only) {
+    wm::RopeParams p;
+    memset(&p, 0, sizeof p);
+    fill_tables_ptrs(r, &p);
+    p.x = k_raw;
+    p.vsrc = v;
+    p.y = reinterpret_cast<uint16_t*>(r->pool + r->L.k_off);
+    p.vdst = reinterpret_cast<uint16_t*>(r->pool + r->L.v_off);
+    p.n_heads = r->desc.n_kv_heads;
+    p.x_b_stride = (int64_t)n_frames * r->ft * r->desc.n_kv_heads * r->desc.head_dim;
+    for (int b = 0; b < B; ++b) {
+      if (!is_active(active, b)) continue;
+      for (int j = 0; j < n_frames; ++j) {
+        const Planned& pl = plan[(size_t)b * n_frames + j];
+        if (!pl.stored) continue;
+        wm::RopeRow& row = p.rows[p.n_rows];
+        row.b = b;
+        row.j = j;
+        row.slot = pl.slot;
+        t_row(r, reps[b].t[j], p.tcos[p.n_rows], p.tsin[p.n_rows]);
+        if (++p.n_rows == wm::kRopeRows) {
+          hipError_t e = wm::launch_kv_append(p, s);
+          if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+          p.n_rows = 0;
+        }
+      }
+    }
+    if (p.n_rows) {
+      hipError_t e = wm::launch_kv_append(p, s);
+      if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+    }
+  }
+  // Commit only once every launch was accepted.
+  for (int b = 0; b < B; ++b)
+    if (is_active(active, b)) r->n_committed[b] += n_frames;
+  if (rep) memcpy(rep, reps.data(), sizeof(wm_append_report) * B);
+  return WM_OK;
+}
+
+wm_status do_attn(const wm_kvring* r, const wm_bf16* q, const wm_bf16* kc, const wm_bf16* vc,
+                  int n_frames, const uint8_t* active, float scale, wm_bf16* out, void* ws,
+                  size_t ws_bytes, hipStream_t s) {
+  (void)ws;
+  (void)ws_bytes;
+  const wm_kvring_desc& d = r->desc;
+  wm::AttnParams p;
+  memset(&p, 0, sizeof p);
+  p.q = q;
+  p.kc = kc;
+  p.vc = vc;
+  p.pk = reinterpret_cast<const uint16_t*>(r->pool + r->L.k_off);
+  p.pv = reinterpret_cast<const uint16_t*>(r->pool + r->L.v_off);
+  p.out = out;
+  p.hq = d.n_q_heads;
+  p.hkv = d.n_kv_heads;
+  p.group = d.n_q_heads / d.n_kv_heads;
+  p.ft = r->ft;
+  p.nq = n_frames * r->ft;
+  p.ring_slots = r->R;
+  p.nqb = (p.nq + 63) / 64;
+  p.wg_per_bg = (p.group * p.nqb + 3) / 4;
+  p.nsplit = 1;
+  const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)d.head_dim));
+  p.scale_log2e = (float)((double)sc * 1.4426950408889634);
+  for (int b = 0; b < d.batch; ++b) {
+    if (!is_active(active, b)) continue;
+    p.b_index[p.nb] = b;
+    p.n_ring[p.nb] = (int32_t)std::min<int64_t>(r->n_committed[b], r->R);
+    if (++p.nb == wm::kAttnMaxB) {
+      hipError_t e = wm::launch_chunk_attn(p, d.head_dim, s);
+      if (e != hipSuccess) return hip_fail(e, "chunk_attn launch");
+      p.nb = 0;
+    }
+  }
+  if (p.nb) {
+    hipError_t e = wm::launch_chunk_attn(p, d.head_dim, s);
+    if (e != hipSuccess) return hip_fail(e, "chunk_attn launch");
+  }
+  return WM_OK;
+}
+
+wm_status check_frames(const wm_kvring* r, int n_frames) {
+  if (n_frames < 1 || n_frames > r->desc.max_chunk)
+    return fail(WM_E_SHAPE, "n_frames %d not in [1, max_chunk=%d]", n_frames, r->desc.max_chunk);
+  return WM_OK;
+}
+
+wm_status check_device_ring(const wm_kvring* r) {
+  if (r->meta_only) return fail(WM_E_STATE, "metadata-only ring has no device pool");
+  return WM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wm_kvring_pool_bytes(const wm_kvring_desc* desc) {
+  Bands b;
+  if (check_desc(desc, &b) != WM_OK) return 0;
+  return layout_of(*desc, b).total;
+}
+
+wm_status wm_kvring_create(const wm_kvring_desc* desc, void* dev_pool, size_t pool_bytes,
+                           wm_kvring** out) {
+  if (!out) return fail(WM_E_ARG, "out is NULL");
+  Bands bands;
+  wm_status st = check_desc(desc, &bands);
+  if (st != WM_OK) return st;
+  const Layout L = layout_of(*desc, bands);
+  const bool meta = dev_pool == nullptr && pool_bytes == 0;
+  if (!meta) {
+    if (!dev_pool) return fail(WM_E_ARG, "dev_pool is NULL but pool_bytes is not 0");
+    if (!aligned16(dev_pool)) return fail(WM_E_ARG, "dev_pool is not 16-byte aligned");
+    if (pool_bytes < L.total)
+      return fail(WM_E_CAPACITY, "pool of %zu bytes, ring needs %zu", pool_bytes, L.total);
+  }
+  wm_kvring* r = new wm_kvring();
+  r->desc = *desc;
+  r->bands = bands;
+  r->L = L;
+  r->ft = desc->frame_h * desc->frame_w;
+  r->R = desc->n_sink + desc->window;
+  r->meta_only = meta;
+  r->pool = static_cast<uint8_t*>(dev_pool);
+  r->n_committed.assign(desc->batch, 0);
+  r->t0.assign(desc->batch, 0);
+  for (int j = 0; j < bands.dt / 2; ++j) r->inv_t.push_back(inv_freq(desc->rope_theta, j, bands.dt));
+  if (!meta && L.tab_bytes) {
+    std::vector<uint8_t> host(L.tab_bytes, 0);
+    auto fill = [&](size_t coff, size_t soff, int n_pos, int da) {
+      float* c = reinterpret_cast<float*>(host.data() + (coff - L.tab_off));
+      float* s = reinterpret_cast<float*>(host.data() + (soff - L.tab_off));
+      for (int pos = 0; pos < n_pos; ++pos)
+        for (int j = 0; j < da / 2; ++j) {
+          const double ang = (double)pos * inv_freq(desc->rope_theta, j, da);
+          c[pos * (da / 2) + j] = (float)g_cos(ang);
+          s[pos * (da / 2) + j] = (float)g_sin(ang);
+        }
+    };
+    fill(L.hcos, L.hsin, desc->frame_h, bands.dh);
+    fill(L.wcos, L.wsin, desc->frame_w, bands.dw);
+    hipError_t e = hipMemcpy(r->pool + L.tab_off, host.data(), L.tab_bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      delete r;
+      return hip_fail(e, "table upload");
+    }
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_live.insert(r);
+  }
+  *out = r;
+  return ok();
+}
+
+wm_status wm_kvring_destroy(wm_kvring* ring) {
+  wm_status st = check_ring(ring);
+  if (st != WM_OK) return st;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_live.erase(ring);
+  }
+  delete ring;
+  return ok();
+}
+
+wm_status wm_kvring_reset(wm_kvring* ring, int32_t b, int64_t t0) {
+  wm_status st = check_ring(ring);
+  if (st != WM_OK) return st;
+  if (b < 0 || b >= ring->desc.batch) return fail(WM_E_ARG, "rollout %d out of range", b);
+  if (t0 < 0 || t0 > ((int64_t)1 << 52)) return fail(WM_E_ARG, "t0 out of range [0, 2^52]");
+  ring->n_committed[b] = 0;
+  ring->t0[b] = t0;
+  return ok();
+}
+
+wm_status wm_kvring_view(const wm_kvring* ring, int32_t b, wm_ring_view* out) {
+  wm_status st = check_ring(ring);
+  if (st != WM_OK) return st;
+  if (!out) return fail(WM_E_ARG, "out is NULL");
+  if (b < 0 || b >= ring->desc.batch) return fail(WM_E_ARG, "rollout %d out of range", b);
+  const int64_t S = ring->desc.n_sink, W = ring->desc.window, m = ring->n_committed[b];
+  memset(out, 0, sizeof *out);
+  int n = 0;
+  for (int64_t f = 0; f < std::min(S, m); ++f) {
+    out->frame[n] = f;
+    out->slot[n] = (int32_t)f;
+    out->t[n] = ring->t0[b] + f;
+    ++n;
+  }
+  if (W > 0)
+    for (int64_t f = std::max(S, m - W); f < m; ++f) {
+      out->frame[n] = f;
+      out->slot[n] = (int32_t)(S + (f - S) % W);
+      out->t[n] = ring->t0[b] + f;
+      ++n;
+    }
+  out->n_retained = n;
+  out->n_committed = m;
+  out->t0 = ring->t0[b];
+  return ok();
+}
+
+wm_status wm_rope3d(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, int32_t n_heads,
+                    int32_t n_frames, const int64_t* t_first, const uint8_t* active,
+                    void* stream) {
+  wm_status st;
+  if ((st = check_ring(ring)) != WM_OK) return st;
+  if ((st = check_device_ring(ring)) != WM_OK) return st;
+  if ((st = check_dev(x, "x")) != WM_OK) return st;
+  if ((st = check_dev(y, "y")) != WM_OK) return st;
+  if ((st = check_frames(ring, n_frames)) != WM_OK) return st;
+  if (n_heads < 1 || n_heads > 256) return fail(WM_E_SHAPE, "n_heads %d not in [1, 256]", n_heads);
+  if (t_first)
+    for (int b = 0; b < ring->desc.batch; ++b)
+      if (is_active(active, b) && (t_first[b] < 0 || t_first[b] > ((int64_t)1 << 52)))
+        return fail(WM_E_ARG, "t_first[%d] out of range [0, 2^52]", b);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = do_rope(ring, x, y, n_heads, n_frames, t_first, active, s)) != WM_OK) return st;
+  return finish(s);
+}
+
+size_t wm_chunk_attn_workspace_bytes(const wm_kvring* ring, int32_t n_frames) {
+  (void)n_frames;
+  if (check_ring(ring) != WM_OK) return 0;
+  return 0;
+}
+
+wm_status wm_chunk_attn(const wm_kvring* ring, const wm_bf16* q_rot, const wm_bf16* k_rot,
+                        const wm_bf16* v, int32_t n_frames, const uint8_t* active,
+                        float softmax_scale, wm_bf16* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  wm_status st;
+  if ((st = check_ring(ring)) != WM_OK) return st;
+  if ((st = check_device_ring(ring)) != WM_OK) return st;
+  if ((st = check_dev(q_rot, "q_rot")) != WM_OK) return st;
+  if ((st = check_dev(k_rot, "k_rot")) != WM_OK) return st;
+  if ((st = check_dev(v, "v")) != WM_OK) return st;
+  if ((st = check_dev(out, "out")) != WM_OK) return st;
+  if ((st = check_frames(ring, n_frames)) != WM_OK) return st;
+  if (workspace && !aligned16(workspace)) return fail(WM_E_ARG, "workspace is not 16-byte aligned");
+  if (!isfinite(softmax_scale)) return fail(WM_E_ARG, "softmax_scale is not finite");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = do_attn(ring, q_rot, k_rot, v, n_frames, active, softmax_scale, out, workspace,
+               workspace_bytes, s);
+  if (st != WM_OK) return st;
+  return finish(s);
+}
+
+wm_status wm_kvring_append_evict(wm_kvring* ring, const wm_bf16* k_raw, const wm_bf16* v,
+                                 int32_t n_frames, const uint8_t* active,
+                                 wm_append_report* rep, void* stream) {
+  wm_status st;
+  if ((st = check_ring(ring)) != WM_OK) return st;
+  if ((st = check_frames(ring, n_frames)) != WM_OK) return st;
+  if (!ring->meta_only) {
+    if ((st = check_dev(k_raw, "k_raw")) != WM_OK) return st;
+    if ((st = check_dev(v, "v")) != WM_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = do_append(ring, k_raw, v, n_frames, active, rep, s)) != WM_OK) return st;
+  if (ring->meta_only) return ok();
+  return finish(s);
+}
+
+wm_status wm_rollout_step(wm_kvring* ring, int32_t n_denoise, const wm_bf16* const* q,
+                          const wm_bf16* const* k, const wm_bf16* const* v, int32_t n_frames,
+                          const uint8_t* active, wm_bf16* q_rot_scratch, wm_bf16* k_rot_scratch,
+                          wm_bf16* const* out, void* workspace, size_t workspace_bytes,
+                          wm_append_report* rep, void* stream) {
+  wm_status st;
+  if ((st = check_ring(ring)) != WM_OK) return st;
+  if ((st = check_device_ring(ring)) != WM_OK) return st;
+  if ((st = check_frames(ring, n_frames)) != WM_OK) return st;
+  if (n_denoise < 1 || n_denoise > 64) return fail(WM_E_ARG, "n_denoise %d not in [1, 64]", n_denoise);
+  if (!q || !k || !v || !out) return fail(WM_E_ARG, "q/k/v/out pointer arrays must not be NULL");
+  for (int i = 0; i < n_denoise; ++i) {
+    if ((st = check_dev(q[i], "q[s]")) != WM_OK) return st;
+    if ((st = check_dev(k[i], "k[s]")) != WM_OK) return st;
+    if ((st = check_dev(v[i], "v[s]")) != WM_OK) return st;
+    if ((st = check_dev(out[i], "out[s]")) != WM_OK) return st;
+  }
+  if ((st = check_dev(q_rot_scratch, "q_rot_scratch")) != WM_OK) return st;
+  if ((st = check_dev(k_rot_scratch, "k_rot_scratch")) != WM_OK) return st;
+  if (workspace && !aligned16(workspace)) return fail(WM_E_ARG, "workspace is not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const wm_kvring_desc& d = ring->desc;
+  for (int i = 0; i < n_denoise; ++i) {
+    if ((st = do_rope(ring, q[i], q_rot_scratch, d.n_q_heads, n_frames, nullptr, active, s)) != WM_OK)
+      return st;
+    if ((st = do_rope(ring, k[i], k_rot_scratch, d.n_kv_heads, n_frames, nullptr, active, s)) != WM_OK)
+      return st;
+    if ((st = do_attn(ring, q_rot_scratch, k_rot_scratch, v[i], n_frames, active, 0.f, out[i],
+                      workspace, workspace_bytes, s)) != WM_OK)
+      return st;
+  }
+  if ((st = do_append(ring, k[n_denoise - 1], v[n_denoise - 1], n_frames, active, rep, s)) != WM_OK)
+    return st;
+  return finish(s);
+}
+
+const char* wm_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Internal interface between the host runtime (wm_api.cpp) and the HIP
+// kernels (kernels/*.hip).  Kernel parameters travel by value as kernel
+// arguments; everything here is plain data.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wm {
+
+// ---------------------------------------------------------------------------
+// RoPE / append
+// ---------------------------------------------------------------------------
+constexpr int kRopeRows = 8;     // (rollout, frame) rows per launch
+constexpr int kMaxTPairs = 32;   // d_t / 2 upper bound
+
+struct RopeRow {
+  int32_t b;      // rollout index
+  int32_t j;      // frame index within the chunk
+  int32_t slot;   // append: destination ring slot (-1: not stored); rope: unused
+  int32_t pad;
+};
+
+struct RopeParams {
+  const uint16_t* x;      // rope: input chunk;  append: unrotated K of the chunk
+  uint16_t* y;            // rope: output chunk; append: K half of the pool
+  const uint16_t* vsrc;   // append only: V of the chunk
+  uint16_t* vdst;         // append only: V half of the pool
+  const float* hcos;      // [frame_h][dh2]
+  const float* hsin;
+  const float* wcos;      // [frame_w][dw2]
+  const float* wsin;
+  int64_t x_b_stride;     // elements per rollout in x / y (rope) or x / vsrc (append)
+  int32_t n_heads;        // heads of x
+  int32_t d;              // head dim
+  int32_t ft;             // tokens per frame
+  int32_t fw;             // frame width
+  int32_t dt2, dh2, dw2;  // pairs per band
+  int32_t ring_slots;     // S + W (append)
+  int32_t n_rows;
+  RopeRow rows[kRopeRows];
+  float tcos[kRopeRows][kMaxTPairs];
+  float tsin[kRopeRows][kMaxTPairs];
+};
+
+hipError_t launch_rope3d(const RopeParams& p, hipStream_t s);
+hipError_t launch_kv_append(const RopeParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Chunk attention
+// ---------------------------------------------------------------------------
+constexpr int kAttnMaxB = 64;    // rollouts per launch
+
+struct AttnParams {
+  const uint16_t* q;      // [B][Nq][Hq][d]
+  const uint16_t* kc;     // [B][Nq][Hkv][d] chunk keys (rotated)
+  const uint16_t* vc;     // [B][Nq][Hkv][d]
+  const uint16_t* pk;     // pool K half [B][R][Hkv][Ft][d]
+  const uint16_t* pv;     // pool V half
+  uint16_t* out;          // [B][Nq][Hq][d]
+  float* part_o;          // split-KV partial outputs (nullptr: no split)
+  float* part_ml;         // split-KV (max, sum) per row
+  int32_t hq, hkv, group; // group = Hq / Hkv
+  int32_t ft;             // tokens per frame
+  int32_t nq;             // queries per rollout = n_frames * Ft
+  int32_t ring_slots;     // R = S + W
+  int32_t nqb;            // 64-query blocks per rollout
+  int32_t wg_per_bg;      // workgroups per (rollout, kv head) per split
+  int32_t nsplit;         // key-range splits (1 = none)
+  float scale_log2e;      // softmax scale * log2(e)
+  int32_t nb;             // rollouts in this launch
+  int32_t b_index[kAttnMaxB];
+  int32_t n_ring[kAttnMaxB];   // visible ring frames (slots 0 .. n_ring-1)
+};
+
+hipError_t launch_chunk_attn(const AttnParams& p, int head_dim, hipStream_t s);
+
+}  // namespace wm

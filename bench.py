@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark of the streaming chunk-attention hot path on one MI355X.
+
+One "step" is one generated chunk at steady state (window full): for each
+of the D denoise steps, 3D-RoPE of Q and K plus chunk attention over sinks +
+window + the chunk, then the RoPE-fused append that commits the chunk and
+evicts the oldest frames -- one wm_rollout_step call.  Default workload: the
+Self-Forcing 1.3B DiT layer shape (12 heads, d 128, 30x52 tokens/frame,
+chunk 3 frames, 1 sink + 18-frame window, 4 denoise steps), synthetic
+N(0,1) bf16 inputs resident in HBM.
+
+Printed: one JSON line.  `value` is whole-step attention throughput
+(algorithmic attention flops of the timed steps / wall time of the timed
+region, RoPE and append included).  `roofline` is the attention kernel alone
+(algorithmic flops per launch / mean launch time from HIP events on the
+launch stream) against the bf16 dense MFMA peak.  `cpu_baseline` times the
+fp64 CPU oracle on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunk-attention TFLOP/s (% bf16 MFMA peak) + denoise-steps/sec per chunk"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, help="workload id (1-5), default 2")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4, help="q heads in the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, n_heads):
+    """Oracle, as it stands, on one steady-state denoise step restricted to n_heads q heads."""
+    import numpy as np
+    from oracle.rollout import Rollout
+    from wm_synth import Source
+
+    src = Source(wl)
+    ro = Rollout(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w, wl.n_sink, wl.window)
+    for n0 in range(wl.n_sink + wl.window):
+        ro.commit(src.chunk(0, n0, 1, -1, "k"), src.chunk(0, n0, 1, -1, "v"), 1)
+    n = wl.chunk
+    n0 = ro.n_committed
+    q = src.chunk(0, n0, n, 0, "q")
+    k = src.chunk(0, n0, n, 0, "k")
+    v = src.chunk(0, n0, n, 0, "v")
+    heads = list(range(min(n_heads, wl.n_q_heads)))
+    t0 = time.perf_counter()
+    q_rot = ro.rope(q, n)
+    k_rot = ro.rope(k, n)
+    ro.attend(q_rot, k_rot, v, n, heads=heads)
+    dt = time.perf_counter() - t0
+    flops = wl.attn_flops() * len(heads) / wl.n_q_heads
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    cores = threads or len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "one steady-state denoise step of %s (RoPE of the chunk's Q and K, attention "
+                      "of all %d queries over %d keys) for %d of %d q heads, fp64 NumPy; %.1f s"
+                      % (wl.name, wl.nq, wl.steady_keys(), len(heads), wl.n_q_heads, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (it would shard by rollout "
+              "or by kv head with no collective in the path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import autoregressive_video_world_amd as wm
+    from wm_synth import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    if wl.batch != 1:
+        print("bench.py times single-rollout workloads (1-4)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + wl.cfg)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    ring = wm.KVRing(1, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                     wl.n_sink, wl.window, wl.chunk, device=dev)
+    C, D, ft = wl.chunk, wl.n_denoise, wl.ft
+    # steady state: fill sinks + window (prefill-style appends of synthetic K/V)
+    filled = 0
+    while filled < wl.n_sink + wl.window:
+        n = min(C, wl.n_sink + wl.window - filled)
+        ring.append_evict(randn(1, n * ft, wl.n_kv_heads, wl.head_dim),
+                          randn(1, n * ft, wl.n_kv_heads, wl.head_dim), n)
+        filled += n
+    qs = [randn(1, C * ft, wl.n_q_heads, wl.head_dim) for _ in range(D)]
+    ks = [randn(1, C * ft, wl.n_kv_heads, wl.head_dim) for _ in range(D)]
+    vs = [randn(1, C * ft, wl.n_kv_heads, wl.head_dim) for _ in range(D)]
+    outs = [torch.empty_like(q) for q in qs]
+    q_rot = torch.empty_like(qs[0])
+    k_rot = torch.empty_like(ks[0])
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ring.rollout_step(qs, ks, vs, C, outs=outs, q_rot_scratch=q_rot, k_rot_scratch=k_rot)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    attn_flops_step = wl.attn_flops() * D
+    value = attn_flops_step * args.steps / elapsed / 1e12
+
+    # ---- per-kernel timing with HIP events on the launch stream ------------
+    def timed(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        return sum(ts) / len(ts), ts[len(ts) // 2]
+
+    ring.rope3d(qs[0], C, y=q_rot)
+    ring.rope3d(ks[0], C, y=k_rot)
+    attn_mean, attn_med = timed(lambda: ring.chunk_attn(q_rot, k_rot, vs[0], C, out=outs[0]),
+                                args.kernel_reps)
+    rope_q_mean, _ = timed(lambda: ring.rope3d(qs[0], C, y=q_rot), args.kernel_reps)
+    rope_k_mean, _ = timed(lambda: ring.rope3d(ks[0], C, y=k_rot), args.kernel_reps)
+    app_mean, app_med = timed(lambda: ring.append_evict(ks[-1], vs[-1], C), args.kernel_reps)
+    torch.cuda.synchronize()
+
+    attn_tflops = wl.attn_flops() / (attn_mean * 1e-3) / 1e12
+    app_bytes = wl.append_bytes()
+    app_gbs = app_bytes / (app_mean * 1e-3) / 1e9
+    rope_bytes = 2 * wl.nq * wl.head_dim * 2 * (wl.n_q_heads + wl.n_kv_heads)
+    rope_gbs = rope_bytes / ((rope_q_mean + rope_k_mean) * 1e-3) / 1e9
+    prof_traffic = None  # filled from rocprofv3 --pmc runs (profiles/), not live
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: %d q/%d kv heads, d %d, %dx%d tokens/frame, chunk %d frames "
+                               "(Nq %d), %d sink + %d window frames (Nk %d), %d denoise steps, steady state"
+                               % (wl.name, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h,
+                                  wl.frame_w, C, wl.nq, wl.n_sink, wl.window, wl.steady_keys(), D),
+                   "batch": 1, "n_q": wl.nq, "n_k": wl.steady_keys(), "denoise_steps": D},
+        "denoise_steps_per_s_per_chunk": round(1e3 / (attn_mean + rope_q_mean + rope_k_mean), 2),
+        "chunks_per_s": round(1e3 / ms_per_step, 3),
+        "attn_pct_mfma_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "chunk_attn_kernel<128>",
+                     "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": prof_traffic,
+                     "launch_ms_mean": round(attn_mean, 4), "launch_ms_median": round(attn_med, 4),
+                     "flops_per_launch": wl.attn_flops()},
+        "append": {"bound": "hbm", "achieved": round(app_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": round(app_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": app_bytes,
+                   "launch_ms_mean": round(app_mean, 5), "launch_ms_median": round(app_med, 5)},
+        "rope": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
+                 "launch_ms_mean_q": round(rope_q_mean, 5), "launch_ms_mean_k": round(rope_k_mean, 5)},
+        "cpu_baseline": None,
+    }
+    ring.close()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)
+    try:
+        result["git"] = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short", "HEAD"],
+                                       capture_output=True, text=True).stdout.strip() or None
+    except Exception:
+        pass
+    result["versions"] = {"torch": torch.__version__, "hip": torch.version.hip}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,243 @@
+/*
+ * wm.h -- streaming block-causal chunk attention over a bounded KV ring,
+ *         for AMD Instinct MI355X (gfx950).
+ *
+ * One layer of the attention of a streaming autoregressive video world
+ * model.  Each generated chunk of latent frames is denoised in a few steps;
+ * in every step the chunk's queries attend, bidirectionally, to the chunk's
+ * own keys and to a bounded cache of earlier frames: S persistent "sink"
+ * (reference) frames plus a FIFO window of the W most recent frames.  After
+ * the last step the chunk's K (rotated by 3D-RoPE at its absolute (t,h,w)
+ * position) and V are appended to the cache and the oldest window frames are
+ * evicted, so device memory stays flat over arbitrarily long rollouts.
+ *
+ * Sources (web pages; section names given):
+ *  - FlashDreams blog post ("NVIDIA FlashDreams Is the Open-Source Inference
+ *    Engine Robotics World Models Needed"), "Bounded Memory for Infinite
+ *    Rollouts": a per-rollout cache with bounded VRAM and internal eviction;
+ *    "Hot-Path Generation, Background State Updates": each step splits into
+ *    generate() (denoising) and finalize() (KV-cache update).
+ *  - Cosmos3-H-Dreams model card, "Model Architecture": block-causal few-step
+ *    student with a KV cache; the conditioning frame is prefilled once;
+ *    "Software Integration": static-shape KV cache, BF16.
+ *  - AlpaDreams GTC write-up, section VII: the causal DiT produces the next
+ *    frame from the historical clean frames and the current noisy frame.
+ *  - DreamZero single-GPU page, "Sequential requests": frame positions and the
+ *    cache persist across requests; explicit start frame / cache reset.
+ *
+ * Conventions that the pages leave open (cache reading, RoPE convention,
+ * rounding) are fixed as documented at each call below.
+ *
+ * General rules
+ *  - Every device pointer is a HIP device address, 16-byte aligned.
+ *  - bf16 tensors are raw IEEE bfloat16 bit patterns (wm_bf16).
+ *  - Token tensors are [B][n_frames*Ft][H][d] (row-major), token index =
+ *    frame*Ft + h*frame_w + w, B = desc.batch (every rollout has a row block,
+ *    active or not).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every launch of a
+ *    call goes onto that stream; no call synchronizes the device or copies
+ *    device data to the host (wm_kvring_create aside).
+ *  - The library allocates no device memory.  The caller owns the pool, all
+ *    tensors, workspaces, host report/view structs and streams.
+ *  - Errors: every argument is validated before anything is enqueued.  A
+ *    non-zero status means nothing was enqueued and the ring is unchanged;
+ *    wm_last_error() then returns a message (thread-local).  Device faults are
+ *    asynchronous and surface at the caller's next synchronization; with the
+ *    environment variable WM_SYNC_CHECK=1 every call synchronizes its stream
+ *    and reports such errors as WM_E_HIP.
+ *  - A ring is not thread-safe; calls on one ring must be ordered on one
+ *    stream (or by the caller's events).
+ */
+#ifndef WM_H_
+#define WM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WM_MAX_CHUNK 16  /* frames per chunk (append / attention call)      */
+#define WM_MAX_RING 256  /* sink + window slots per rollout                 */
+#define WM_MAX_BATCH 1024
+
+typedef uint16_t wm_bf16;
+typedef struct wm_kvring wm_kvring;
+
+typedef enum {
+  WM_OK = 0,
+  WM_E_ARG = 1,         /* NULL / misaligned pointer, out-of-range scalar   */
+  WM_E_SHAPE = 2,       /* shape not allowed by the ring's descriptor      */
+  WM_E_STATE = 3,       /* destroyed handle, metadata-only ring, bad state */
+  WM_E_CAPACITY = 4,    /* pool or workspace too small                     */
+  WM_E_HIP = 5,         /* a HIP call failed                               */
+  WM_E_UNSUPPORTED = 6  /* valid request this build does not implement     */
+} wm_status;
+
+typedef struct {
+  int32_t batch;        /* B >= 1 independent rollouts (no cross-rollout attention)   */
+  int32_t n_q_heads;    /* Hq >= 1                                                    */
+  int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0; q head h reads kv head h/(Hq/Hkv) */
+  int32_t head_dim;     /* d: 64 or 128                                               */
+  int32_t frame_h;      /* latent grid height                                         */
+  int32_t frame_w;      /* latent grid width; Ft = frame_h*frame_w tokens per frame   */
+  int32_t n_sink;       /* S >= 0: the first S frames of a sequence, never evicted    */
+  int32_t window;       /* W >= 0: FIFO window of the most recent later frames        */
+  int32_t max_chunk;    /* C in [1, WM_MAX_CHUNK]: frames per call                    */
+  double rope_theta;    /* RoPE base (e.g. 10000.0), > 1                              */
+  int32_t rope_dims[3]; /* {d_t,d_h,d_w} even, sum d; {0,0,0} = default split:
+                           d_h = d_w = 2*floor(d/6), d_t = d - d_h - d_w             */
+} wm_kvring_desc;
+
+/* Per-rollout result of one append, in commit order.  A frame that is
+ * committed but not stored (W == 0 and not a sink, or pushed out again by a
+ * later frame of the same append) still appears in frame/slot/t; slot is -1
+ * when it is never stored, and it is listed in `evicted` when a later frame
+ * of the same append pushes it out. */
+typedef struct {
+  int32_t n_written;                 /* frames committed by this append       */
+  int32_t n_evicted;                 /* frames evicted by this append         */
+  int64_t frame[WM_MAX_CHUNK];       /* frame id within the sequence          */
+  int32_t slot[WM_MAX_CHUNK];        /* ring slot it was assigned, or -1      */
+  int64_t t[WM_MAX_CHUNK];           /* absolute temporal position t0 + frame */
+  int64_t evicted[WM_MAX_CHUNK];     /* evicted frame ids, oldest first       */
+} wm_append_report;
+
+/* Frames a rollout holds, in temporal order. */
+typedef struct {
+  int32_t n_retained;
+  int64_t frame[WM_MAX_RING];
+  int32_t slot[WM_MAX_RING];
+  int64_t t[WM_MAX_RING];
+  int64_t n_committed;               /* frames committed since the last reset */
+  int64_t t0;                        /* temporal origin of the sequence       */
+} wm_ring_view;
+
+/* ---------------------------------------------------------------------------
+ * Pool
+ *
+ * Bytes of device memory a ring needs (0 if the descriptor is invalid).
+ * Layout, all offsets from the pool base:
+ *   K half : bf16 [B][S+W][Hkv][Ft][d]   -- each (slot, kv head) one
+ *                                           contiguous Ft x d block
+ *   V half : bf16 [B][S+W][Hkv][Ft][d]   -- at offset K-half bytes
+ *   tables : fp32 cos/sin rows of the h and w RoPE bands, 256-byte aligned
+ * Slot of frame f of a sequence: f if f < S, else S + (f - S) mod W.
+ */
+size_t wm_kvring_pool_bytes(const wm_kvring_desc* desc);
+
+/* Create a ring over a caller-owned device pool of at least
+ * wm_kvring_pool_bytes(desc) bytes (16-byte aligned, valid until destroy).
+ * Writes the RoPE h/w tables into the pool's table area with a synchronous
+ * host-to-device copy; K/V slot contents are left as they are.  Every
+ * rollout starts empty at t0 = 0.
+ * dev_pool == NULL with pool_bytes == 0 creates a metadata-only ring: appends
+ * update the bookkeeping and reports only (no device access), and
+ * wm_rope3d / wm_chunk_attn / wm_rollout_step return WM_E_STATE.
+ * Errors: WM_E_ARG (NULL desc/out, misaligned pool), WM_E_SHAPE (invalid
+ * descriptor), WM_E_CAPACITY (pool too small), WM_E_HIP. */
+wm_status wm_kvring_create(const wm_kvring_desc* desc, void* dev_pool, size_t pool_bytes,
+                           wm_kvring** out);
+
+/* Release the handle (host memory only; the pool stays the caller's).
+ * Calls with a destroyed handle return WM_E_STATE. */
+wm_status wm_kvring_destroy(wm_kvring* ring);
+
+/* Start a new sequence on rollout b: no frames committed, temporal origin
+ * t0 (DreamZero page, "Sequential requests": current start frame and cache
+ * reset).  Old slot contents are simply no longer visible. */
+wm_status wm_kvring_reset(wm_kvring* ring, int32_t b, int64_t t0);
+
+/* Retained frames of rollout b in temporal order (sinks, then window). */
+wm_status wm_kvring_view(const wm_kvring* ring, int32_t b, wm_ring_view* out);
+
+/* ---------------------------------------------------------------------------
+ * 3D-RoPE of a chunk's Q or K (one denoise step).
+ *
+ * x, y : bf16 [B][n_frames*Ft][n_heads][d] (y may equal x).  Token r of chunk
+ * frame j of rollout b sits at t = t_first[b] + j, h = (r mod Ft) / frame_w,
+ * w = r mod frame_w; t_first == NULL means each rollout's next uncommitted
+ * frame (t0 + n_committed).  Bands [t | h | w] of the head dim; in a band of
+ * width d_a, pair j = elements (2j, 2j+1) rotated by angle pos*theta^(-2j/d_a);
+ * cos/sin are libm fp64 values rounded once to fp32 (computed on the host);
+ * y0 = x0*c - x1*s, y1 = x0*s + x1*c in fp64 (the products are exact), then
+ * rounded to bf16 round-to-nearest-even.  Only active rollouts (active[b] !=
+ * 0; NULL = all) are read or written.
+ * Errors: WM_E_ARG, WM_E_SHAPE (n_frames not in [1, max_chunk], n_heads < 1),
+ * WM_E_STATE (metadata-only ring), WM_E_HIP. */
+wm_status wm_rope3d(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, int32_t n_heads,
+                    int32_t n_frames, const int64_t* t_first, const uint8_t* active, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Chunk attention (one denoise step; FlashDreams generate()).
+ *
+ * For every active rollout b and q head h (kv head g = h / (Hq/Hkv)):
+ *   out[b,i,h,:] = softmax_j( q_rot[b,i,h,:] . K_j / scale^-1 ) V_j
+ * over the keys j of: the sink frames and window frames rollout b holds
+ * (committed K_rot/V in the pool) and all n_frames frames of the chunk itself
+ * (k_rot, v of this step) -- bidirectional inside the chunk, no other mask.
+ * q_rot : bf16 [B][n_frames*Ft][Hq][d]     (already rotated, see wm_rope3d)
+ * k_rot : bf16 [B][n_frames*Ft][Hkv][d]    (already rotated)
+ * v     : bf16 [B][n_frames*Ft][Hkv][d]
+ * out   : bf16 [B][n_frames*Ft][Hq][d], round-to-nearest-even of the fp32
+ *         result (bf16 MFMA products, fp32 accumulation and softmax).
+ * softmax_scale <= 0 selects 1/sqrt(d).
+ * workspace: optional device scratch for splitting long key ranges across
+ * workgroups (more parallelism when B*Hq*Nq is small); NULL/0 = no split.
+ * wm_chunk_attn_workspace_bytes() gives the size that enables the split.
+ * Errors: WM_E_ARG, WM_E_SHAPE, WM_E_STATE, WM_E_HIP. */
+wm_status wm_chunk_attn(const wm_kvring* ring, const wm_bf16* q_rot, const wm_bf16* k_rot,
+                        const wm_bf16* v, int32_t n_frames, const uint8_t* active,
+                        float softmax_scale, wm_bf16* out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that let wm_chunk_attn split the key range for a chunk of
+ * n_frames frames (0 if splitting never pays for this ring's shapes). */
+size_t wm_chunk_attn_workspace_bytes(const wm_kvring* ring, int32_t n_frames);
+
+/* ---------------------------------------------------------------------------
+ * Append + evict (FlashDreams finalize()).
+ *
+ * Commits n_frames frames to every active rollout: frame ids n_committed ..
+ * n_committed+n_frames-1, t = t0 + id.  K is rotated by the same rule as
+ * wm_rope3d at each frame's t and stored with V in the frame's slot; the
+ * oldest window frames are evicted FIFO; sinks are never evicted.  Frames
+ * that would be evicted again within the same append are not written.
+ * k_raw, v : bf16 [B][n_frames*Ft][Hkv][d] (unrotated K).
+ * rep      : host array [B] or NULL; filled for active rollouts (inactive
+ *            rollouts get n_written = n_evicted = 0).
+ * Bookkeeping is host-side closed form: no device readback.  Stream order
+ * matters: an append overwrites the slot of each frame it evicts, which the
+ * chunk's own attention read, so it must follow that attention on the stream.
+ * Prefill (conditioning frames committed without attention) is this call.
+ * Errors: WM_E_ARG, WM_E_SHAPE, WM_E_HIP. */
+wm_status wm_kvring_append_evict(wm_kvring* ring, const wm_bf16* k_raw, const wm_bf16* v,
+                                 int32_t n_frames, const uint8_t* active,
+                                 wm_append_report* rep, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * One whole chunk: n_denoise x (RoPE of Q and K, chunk attention), then the
+ * append of the last step's K and V.
+ * q[s], k[s], v[s] : host arrays of n_denoise device pointers (step s inputs,
+ *                    unrotated), shapes as in wm_chunk_attn.
+ * q_rot_scratch    : bf16 [B][n_frames*Ft][Hq][d] device scratch
+ * k_rot_scratch    : bf16 [B][n_frames*Ft][Hkv][d] device scratch
+ * out[s]           : host array of n_denoise device output pointers.
+ * workspace        : as for wm_chunk_attn.
+ * rep              : as for wm_kvring_append_evict.
+ * Errors: as the calls it makes; validation of everything happens first. */
+wm_status wm_rollout_step(wm_kvring* ring, int32_t n_denoise, const wm_bf16* const* q,
+                          const wm_bf16* const* k, const wm_bf16* const* v, int32_t n_frames,
+                          const uint8_t* active, wm_bf16* q_rot_scratch, wm_bf16* k_rot_scratch,
+                          wm_bf16* const* out, void* workspace, size_t workspace_bytes,
+                          wm_append_report* rep, void* stream);
+
+/* Thread-local message for the last non-OK status ("" if none). */
+const char* wm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WM_H_ */

@@ -1,0 +1,223 @@
+"""C-ABI checks that need no GPU.
+
+* libwm.so loads and exports every function include/wm.h declares;
+* the host bookkeeping (slots, positions, evictions, retained frames) of a
+  metadata-only ring equals the oracle's deque ring, bit for bit, on every
+  workload -- including 8 staggered rollouts of 10,000 frames;
+* argument validation returns the documented status before any HIP call and
+  leaves the ring unchanged.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import autoregressive_video_world_amd as wm
+from autoregressive_video_world_amd import binding
+from oracle.ring import DequeRing
+from wm_synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "wm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    decl = declared_functions()
+    assert decl == sorted(binding.EXPORTS)
+    L = wm.lib()
+    for name in decl:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (wm_\w+)", out))
+    assert set(decl) <= exported
+
+
+def ring_for(wl, meta=True):
+    return wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                     wl.n_sink, wl.window, wl.chunk, meta_only=meta)
+
+
+def test_pool_bytes_formula():
+    for wl in WORKLOADS.values():
+        r = ring_for(wl)
+        half = wl.batch * (wl.n_sink + wl.window) * wl.n_kv_heads * wl.ft * wl.head_dim * 2
+        assert r.pool_bytes >= 2 * half
+        assert r.pool_bytes - 2 * half < 2 * 256 + 4 * 4 * (wl.frame_h + wl.frame_w) * wl.head_dim
+        assert r.pool_bytes % 256 == 0
+        r.close()
+
+
+def oracle_append(dq, n, t0):
+    written, evicted = [], []
+    for _ in range(n):
+        f, s, ev = dq.commit()
+        written.append((f, s, t0 + f))
+        evicted.extend(ev)
+    return {"written": written, "evicted": evicted}
+
+
+def view_of(dq, t0):
+    return [(f, s, t0 + f) for f, s in dq.retained()]
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_bookkeeping_matches_oracle(cfg):
+    wl = WORKLOADS[cfg]
+    r = ring_for(wl)
+    dq = DequeRing(wl.n_sink, wl.window)
+    if wl.prefill:
+        assert r.append_evict(None, None, wl.prefill) == [oracle_append(dq, wl.prefill, 0)]
+    for c in wl.chunks():
+        assert r.view(0)["retained"] == view_of(dq, 0)
+        assert r.append_evict(None, None, c) == [oracle_append(dq, c, 0)]
+    v = r.view(0)
+    assert v["retained"] == view_of(dq, 0)
+    assert v["n_committed"] == wl.prefill + wl.n_gen
+    r.close()
+
+
+@pytest.mark.slow
+def test_long_staggered_rollouts_match_oracle():
+    """8 rollouts x (1 prefill + 10,000 frames), rollout b admitted at step 7b."""
+    wl = WORKLOADS[5]
+    r = ring_for(wl)
+    dqs = [DequeRing(wl.n_sink, wl.window) for _ in range(wl.batch)]
+    last_step = wl.stagger * (wl.batch - 1) + wl.n_gen
+    max_t = 0
+    for g in range(last_step + 1):
+        active = [0 <= g - wl.stagger * b <= wl.n_gen for b in range(wl.batch)]
+        reps = r.append_evict(None, None, 1, active=active)
+        for b in range(wl.batch):
+            if active[b]:
+                want = oracle_append(dqs[b], 1, 0)
+                assert reps[b] == want, (g, b)
+                max_t = max(max_t, want["written"][0][2])
+            else:
+                assert reps[b] == {"written": [], "evicted": []}
+            if g % 97 == 0 or g == last_step:
+                assert r.view(b)["retained"] == view_of(dqs[b], 0)
+    for b in range(wl.batch):
+        v = r.view(b)
+        assert v["n_committed"] == wl.n_gen + 1
+        assert len(v["retained"]) == wl.n_sink + wl.window
+        assert v["retained"][-1][2] == 10_000
+    assert max_t == 10_000
+
+
+def test_reset_and_origin():
+    wl = WORKLOADS[3]
+    r = ring_for(wl)
+    for _ in range(6):
+        r.append_evict(None, None, 1)
+    r.reset(0, t0=1000)
+    assert r.view(0) == {"retained": [], "n_committed": 0, "t0": 1000}
+    rep = r.append_evict(None, None, 1)
+    assert rep[0]["written"] == [(0, 0, 1000)]
+    r.close()
+
+
+def test_chunk_longer_than_window():
+    """Frames pushed out by later frames of the same append are reported evicted."""
+    r = wm.KVRing(1, 2, 2, 64, 2, 2, 1, 2, 5, meta_only=True)
+    dq = DequeRing(1, 2)
+    assert r.append_evict(None, None, 5) == [oracle_append(dq, 5, 0)]
+    assert r.append_evict(None, None, 5) == [oracle_append(dq, 5, 0)]
+    assert r.view(0)["retained"] == view_of(dq, 0)
+    r.close()
+
+
+def test_zero_window_stores_sinks_only():
+    r = wm.KVRing(1, 2, 2, 64, 2, 2, 2, 0, 3, meta_only=True)
+    dq = DequeRing(2, 0)
+    for _ in range(3):
+        assert r.append_evict(None, None, 3) == [oracle_append(dq, 3, 0)]
+    assert [s for _, s, _ in r.view(0)["retained"]] == [0, 1]
+    r.close()
+
+
+# ---------------------------------------------------------------------------
+# validation and error codes (no HIP call is reached)
+# ---------------------------------------------------------------------------
+def make_desc(**kw):
+    base = dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=128, frame_h=4, frame_w=5, n_sink=1,
+                window=3, max_chunk=2, rope_theta=10000.0)
+    base.update(kw)
+    dims = base.pop("rope_dims", (0, 0, 0))
+    return binding.Desc(**base, rope_dims=(ctypes.c_int32 * 3)(*dims))
+
+
+@pytest.mark.parametrize("bad", [dict(n_q_heads=3), dict(head_dim=96), dict(max_chunk=0),
+                                 dict(max_chunk=17), dict(n_sink=200, window=57), dict(batch=0),
+                                 dict(rope_dims=(42, 42, 42)), dict(rope_dims=(43, 43, 42)),
+                                 dict(rope_theta=1.0), dict(frame_w=0), dict(window=-1),
+                                 dict(rope_dims=(128, 0, 0))])
+def test_invalid_descriptor(bad):
+    L = wm.lib()
+    d = make_desc(**bad)
+    assert L.wm_kvring_pool_bytes(ctypes.byref(d)) == 0
+    h = ctypes.c_void_p()
+    st = L.wm_kvring_create(ctypes.byref(d), None, 0, ctypes.byref(h))
+    assert st == 2 and not h.value
+    assert L.wm_last_error()
+
+
+def test_create_argument_errors():
+    L = wm.lib()
+    d = make_desc()
+    need = L.wm_kvring_pool_bytes(ctypes.byref(d))
+    h = ctypes.c_void_p()
+    assert L.wm_kvring_create(ctypes.byref(d), None, 0, None) == 1
+    assert L.wm_kvring_create(None, None, 0, ctypes.byref(h)) == 1
+    # non-NULL but never dereferenced: the checks fail first
+    assert L.wm_kvring_create(ctypes.byref(d), ctypes.c_void_p(0x1008), need, ctypes.byref(h)) == 1
+    assert L.wm_kvring_create(ctypes.byref(d), ctypes.c_void_p(0x1000), need - 1, ctypes.byref(h)) == 4
+    assert L.wm_kvring_create(ctypes.byref(d), None, 64, ctypes.byref(h)) == 1
+    assert b"pool" in L.wm_last_error()
+
+
+def test_call_errors_leave_state_unchanged():
+    L = wm.lib()
+    r = wm.KVRing(2, 4, 2, 128, 4, 5, 1, 3, 2, meta_only=True)
+    r.append_evict(None, None, 2)
+    before = [r.view(b) for b in range(2)]
+    for n in (0, 3, -1):
+        with pytest.raises(wm.WMError) as e:
+            r.append_evict(None, None, n)
+        assert e.value.name == "WM_E_SHAPE"
+    assert [r.view(b) for b in range(2)] == before
+    with pytest.raises(wm.WMError) as e:
+        r.reset(2, 0)
+    assert e.value.name == "WM_E_ARG"
+    # device calls on a metadata-only ring
+    p = ctypes.c_void_p(0x1000)
+    assert L.wm_rope3d(r._h, p, p, 4, 1, None, None, None) == 3
+    assert L.wm_chunk_attn(r._h, p, p, p, 1, None, 0.0, p, None, 0, None) == 3
+    arr = (ctypes.c_void_p * 1)(p)
+    assert L.wm_rollout_step(r._h, 1, arr, arr, arr, 1, None, p, p, arr, None, 0, None, None) == 3
+    assert [r.view(b) for b in range(2)] == before
+    # success clears the message
+    r.view(0)
+    assert L.wm_last_error() == b""
+    r.close()
+
+
+def test_destroyed_handle_is_rejected():
+    L = wm.lib()
+    r = wm.KVRing(1, 2, 2, 64, 2, 2, 1, 1, 1, meta_only=True)
+    h = ctypes.c_void_p(r._h.value)
+    r.close()
+    assert L.wm_kvring_destroy(h) == 3
+    assert L.wm_kvring_reset(h, 0, 0) == 3
+    v = binding.RingView()
+    assert L.wm_kvring_view(h, 0, ctypes.byref(v)) == 3
+    assert L.wm_kvring_append_evict(h, None, None, 1, None, None, None) == 3
+    assert L.wm_kvring_destroy(None) == 1

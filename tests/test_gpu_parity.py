@@ -1,0 +1,245 @@
+"""GPU parity: the HIP library against the fp64 oracle (MI355X).
+
+Small rollouts are compared element by element on every output: RoPE and
+stored K/V bit-exact, reports and slots bit-exact, attention within the
+stated tolerance (tests/gpu_util.py).  The pool is filled with a sentinel
+(0xFFFF) before the ring is created, so a write outside the planned slots
+shows up.  Shapes are chosen to span several 64-query blocks, several 64-key
+tiles, ragged tails, GQA, d = 64 and 128, chunks longer than one frame,
+batches with inactive and staggered rollouts, and windows that wrap.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import autoregressive_video_world_amd as wm
+from oracle.rollout import Rollout
+from oracle import rope as orope
+from wm_synth import Source, Workload, WORKLOADS
+from gpu_util import assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0xFFFF
+
+
+def make_ring(wl, t0s=None):
+    pool_bytes = wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h,
+                           wl.frame_w, wl.n_sink, wl.window, wl.chunk, meta_only=True).pool_bytes
+    pool = torch.full((pool_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    ring = wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                     wl.n_sink, wl.window, wl.chunk, pool=pool)
+    oracles = [Rollout(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                       wl.n_sink, wl.window) for _ in range(wl.batch)]
+    if t0s:
+        for b, t0 in enumerate(t0s):
+            ring.reset(b, t0)
+            oracles[b].reset(t0)
+    return ring, oracles
+
+
+def check_pool(ring, oracles, used_slots):
+    pk = host(ring.pool_k())
+    pv = host(ring.pool_v())
+    for b, ro in enumerate(oracles):
+        for f, slot, t in ro.retained():
+            kb, vb = ro.cache[f]
+            assert np.array_equal(pk[b, slot], kb.transpose(1, 0, 2)), ("K", b, f, slot)
+            assert np.array_equal(pv[b, slot], vb.transpose(1, 0, 2)), ("V", b, f, slot)
+        for slot in range(ring.slots):
+            if slot not in used_slots[b]:
+                assert np.all(pk[b, slot] == SENTINEL) and np.all(pv[b, slot] == SENTINEL), (b, slot)
+
+
+def run_case(wl, t0s=None, use_step=False, q_scale=1.0):
+    """Drive ``wl`` through the library and the oracle; compare everything."""
+    src = Source(wl, q_scale=q_scale)
+    ring, oracles = make_ring(wl, t0s)
+    B, ft = wl.batch, wl.ft
+    actions = [([("prefill", wl.prefill)] if wl.prefill else []) + [("gen", c) for c in wl.chunks()]
+               for _ in range(B)]
+    used = [set() for _ in range(B)]
+    n_steps = max(wl.stagger * b + len(actions[b]) for b in range(B))
+    worst = [0.0, 0.0, 0.0]
+    for g in range(n_steps):
+        groups = {}
+        for b in range(B):
+            k = g - wl.stagger * b
+            if 0 <= k < len(actions[b]):
+                groups.setdefault(actions[b][k], []).append(b)
+        for (kind, n), bs in sorted(groups.items()):
+            active = [b in bs for b in range(B)]
+            n0s = [oracles[b].n_committed if active[b] else None for b in range(B)]
+            if kind == "prefill":
+                k_np = src.batch_chunk(n0s, n, -1, "k")
+                v_np = src.batch_chunk(n0s, n, -1, "v")
+            else:
+                qs, ks, vs, outs_ref = [], [], [], []
+                for s in range(wl.n_denoise):
+                    q_np = src.batch_chunk(n0s, n, s, "q")
+                    k_np = src.batch_chunk(n0s, n, s, "k")
+                    v_np = src.batch_chunk(n0s, n, s, "v")
+                    qs.append(q_np)
+                    ks.append(k_np)
+                    vs.append(v_np)
+                    refs = {}
+                    for b in bs:
+                        refs[b] = oracles[b].denoise_step(q_np[b], k_np[b], v_np[b], n)
+                    outs_ref.append(refs)
+                if use_step:
+                    outs, reps = ring.rollout_step([dev(x) for x in qs], [dev(x) for x in ks],
+                                                   [dev(x) for x in vs], n, active=active)
+                    for s in range(wl.n_denoise):
+                        got = host(outs[s])
+                        for b in bs:
+                            errs = assert_close(got[b], outs_ref[s][b][2], "step %d b %d s %d" % (g, b, s))
+                            worst = [max(a, e) for a, e in zip(worst, errs)]
+                else:
+                    for s in range(wl.n_denoise):
+                        qd, kd, vd = dev(qs[s]), dev(ks[s]), dev(vs[s])
+                        q_rot = ring.rope3d(qd, n, active=active)
+                        k_rot = ring.rope3d(kd, n, active=active)
+                        out = ring.chunk_attn(q_rot, k_rot, vd, n, active=active)
+                        qr, kr, o = host(q_rot), host(k_rot), host(out)
+                        for b in bs:
+                            ref_q, ref_k, ref_o = outs_ref[s][b]
+                            assert np.array_equal(qr[b], ref_q), ("q_rot", g, b, s)
+                            assert np.array_equal(kr[b], ref_k), ("k_rot", g, b, s)
+                            errs = assert_close(o[b], ref_o, "step %d b %d s %d" % (g, b, s))
+                            worst = [max(a, e) for a, e in zip(worst, errs)]
+                k_np, v_np = ks[-1], vs[-1]
+            if kind == "prefill" or not use_step:
+                reps = ring.append_evict(dev(k_np), dev(v_np), n, active=active)
+            for b in range(B):
+                if active[b]:
+                    written, evicted = oracles[b].commit(k_np[b], v_np[b], n)
+                    assert reps[b] == {"written": written, "evicted": evicted}, (g, b)
+                    used[b].update(s for f, s, t in oracles[b].retained())
+                else:
+                    assert reps[b] == {"written": [], "evicted": []}
+            check_pool(ring, oracles, used)
+    for b in range(B):
+        assert ring.view(b)["retained"] == oracles[b].retained()
+    ring.close()
+    return worst
+
+
+def W(cfg, **kw):
+    base = dict(cfg=cfg, name="case%d" % cfg, batch=1, n_q_heads=2, n_kv_heads=2, head_dim=128,
+                frame_h=10, frame_w=10, chunk=1, n_sink=1, window=3, prefill=0, n_gen=6, n_denoise=1)
+    base.update(kw)
+    return Workload(**base)
+
+
+CASES = {
+    "tiny": WORKLOADS[1],
+    "mha_ft100_c2": W(101, chunk=2, n_gen=9, n_denoise=2),
+    "gqa_ft70": W(102, n_q_heads=8, n_kv_heads=2, frame_h=7, frame_w=10, window=2, prefill=1, n_gen=5),
+    "d64_ft50_c3": W(103, head_dim=64, frame_h=5, frame_w=10, chunk=3, window=4, n_gen=10),
+    "batch3_staggered": W(104, batch=3, n_q_heads=4, n_kv_heads=4, frame_h=6, frame_w=7, window=2,
+                          prefill=1, n_gen=5, stagger=2),
+    "no_sink": W(105, n_sink=0, window=2, frame_h=4, frame_w=9, n_gen=5),
+    "no_window": W(106, n_sink=2, window=0, frame_h=3, frame_w=11, chunk=2, n_gen=5),
+    "chunk_gt_window": W(107, n_sink=1, window=2, chunk=4, frame_h=3, frame_w=5, n_gen=9),
+    "gqa8_one_kv_head": W(108, n_q_heads=8, n_kv_heads=1, frame_h=9, frame_w=9, window=2, n_gen=4),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_rollout_parity(name):
+    print("case", name, flush=True)
+    run_case(CASES[name])
+
+
+def test_rollout_parity_sharp_queries():
+    """Q scaled x8: a peaked softmax, where a dropped frame moves O by ~4e-2."""
+    run_case(CASES["mha_ft100_c2"], q_scale=8.0)
+
+
+def test_rollout_parity_absolute_origins():
+    run_case(CASES["batch3_staggered"], t0s=[0, 1000, 9_999])
+
+
+@pytest.mark.parametrize("name", ["tiny", "batch3_staggered", "gqa_ft70"])
+def test_rollout_step_parity(name):
+    run_case(CASES[name], use_step=True)
+
+
+def test_single_key_gives_value_bit_exact():
+    """No cache, one token per frame, one frame: the only key is the token itself."""
+    wl = W(120, n_sink=0, window=0, frame_h=1, frame_w=1, n_gen=2, n_q_heads=4, n_kv_heads=2)
+    src = Source(wl)
+    ring, _ = make_ring(wl)
+    q = dev(src.batch_chunk([0], 1, 0, "q"))
+    k = dev(src.batch_chunk([0], 1, 0, "k"))
+    v_np = src.batch_chunk([0], 1, 0, "v")
+    out = host(ring.chunk_attn(q, k, dev(v_np), 1))
+    # head h reads kv head h // 2
+    for h in range(4):
+        assert np.array_equal(out[0, 0, h], v_np[0, 0, h // 2])
+    ring.close()
+
+
+def test_rope_explicit_t_first_and_inactive_rows_untouched():
+    wl = W(121, batch=3, frame_h=4, frame_w=6)
+    ring, _ = make_ring(wl)
+    src = Source(wl)
+    x = src.batch_chunk([0, 0, 0], 1, 0, "q")
+    y = torch.full(x.shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    ring.rope3d(dev(x), 1, y=y, t_first=[5, 123456, 0], active=[1, 0, 1])
+    got = host(y)
+    for b, t in ((0, 5), (2, 0)):
+        assert np.array_equal(got[b], orope.rotate_frames(x[b], 4, 6, t))
+    assert np.all(got[1] == host(torch.full((1,), 7.0, dtype=torch.bfloat16))[0])
+    ring.close()
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, steady state, sampled outputs
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_full_size_steady_state_sampled(cfg):
+    """Window full, one chunk's denoise step at full size: RoPE bit-exact on the
+    whole chunk, attention on sampled query rows and heads, then the append."""
+    wl = WORKLOADS[cfg]
+    print("full-size workload", wl.name, flush=True)
+    src = Source(wl)
+    ring, oracles = make_ring(wl)
+    ro = oracles[0]
+    # fill sinks + window with prefill-style commits (both sides)
+    n_fill = wl.n_sink + wl.window + 1
+    for n0 in range(n_fill):
+        k_np = src.batch_chunk([n0], 1, -1, "k")
+        v_np = src.batch_chunk([n0], 1, -1, "v")
+        ring.append_evict(dev(k_np), dev(v_np), 1)
+        ro.commit(k_np[0], v_np[0], 1)
+    n = wl.chunk
+    n0 = ro.n_committed
+    q_np = src.batch_chunk([n0], n, 0, "q")
+    k_np = src.batch_chunk([n0], n, 0, "k")
+    v_np = src.batch_chunk([n0], n, 0, "v")
+    q_rot = ring.rope3d(dev(q_np), n)
+    k_rot = ring.rope3d(dev(k_np), n)
+    out = host(ring.chunk_attn(q_rot, k_rot, dev(v_np), n))
+    ref_q = ro.rope(q_np[0], n)
+    ref_k = ro.rope(k_np[0], n)
+    assert np.array_equal(host(q_rot)[0], ref_q)
+    assert np.array_equal(host(k_rot)[0], ref_k)
+    rng = np.random.default_rng(cfg)
+    nq = n * wl.ft
+    rows = np.unique(np.concatenate([np.arange(0, 70), np.arange(nq - 70, nq),
+                                     rng.integers(0, nq, 200)]))
+    heads = sorted({0, wl.n_q_heads - 1, int(rng.integers(0, wl.n_q_heads))})
+    ref = ro.attend(ref_q, ref_k, v_np[0], n, heads=heads, rows=rows)
+    for h in heads:
+        assert_close(out[0][rows][:, h], ref[:, h], "%s head %d" % (wl.name, h))
+    rep = ring.append_evict(dev(k_np), dev(v_np), n)
+    written, evicted = ro.commit(k_np[0], v_np[0], n)
+    assert rep[0] == {"written": written, "evicted": evicted}
+    pk = host(ring.pool_k())
+    for f, slot, t in ro.retained()[-n:]:
+        assert np.array_equal(pk[0, slot], ro.cache[f][0].transpose(1, 0, 2))
+    ring.close()
