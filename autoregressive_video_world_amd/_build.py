@@ -24,6 +24,11 @@ COMMON = [
 ]
 
 
+# Extra flags per source file (relative to csrc/).  The attention kernel is
+# built without NaN semantics so that max() needs no NaN-quieting instructions.
+PER_FILE = {os.path.join("kernels", "chunk_attn.hip"): ["-fno-honor-nans"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.cpp")) +
                   glob.glob(os.path.join(CSRC, "kernels", "*.hip")))
@@ -31,7 +36,7 @@ def sources():
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.relpath(src, CSRC).replace(os.sep, "_") + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + COMMON + PER_FILE.get(os.path.relpath(src, CSRC), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -13,48 +13,64 @@
 //
 // Design (one workgroup = 4 waves = 4 "wave tasks" that share one kv head):
 //  * a wave task is 64 queries of one q head: two 32-query blocks;
-//  * keys stream through LDS in 64-key tiles, double-buffered: while a tile
-//    is consumed from LDS the next one is in flight from HBM/L2 in VGPRs;
-//  * S^T = K * Q^T on v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held
-//    in VGPRs for the whole kernel): in the 32x32 accumulator layout each
-//    lane owns one query column and 16 keys, so the row max / row sum need
-//    one cross-half exchange (v_permlane32_swap) instead of a reduction tree;
+//  * keys stream through LDS in 64-key tiles (K double-, V triple-buffered,
+//    one barrier per tile); tile loads are issued two tiles ahead and are
+//    branch-free: keys past the end are clamped to the last key and masked
+//    out of the softmax;
+//  * S^T = K * Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T
+//    held in registers for the whole kernel): in the 32x32 accumulator
+//    layout each lane owns one query column and 16 keys, so the row max and
+//    row sum need one cross-half exchange (v_permlane32_swap), no tree;
 //  * O^T += V^T * P^T on the same MFMA: P^T comes straight from the S^T
-//    accumulator (exp2, cvt_pk_bf16); V is stored transposed in LDS with the
-//    keys permuted so that each lane's 8 keys are one 16-byte LDS read;
-//  * online softmax in the log2 domain with fp32 running max and sum;
+//    accumulator (exp2, cvt_pk_bf16).  V stays in its natural [key][d] layout
+//    in LDS and the V^T operand is read with ds_read_b64_tr_b16: in each
+//    16-lane group, lane j receives element j%4 of the 8-byte chunks read by
+//    lanes j/4, j/4+4, j/4+8, j/4+12, so when lane L reads row kbase + L/4 at
+//    column dbase + 4*(L%4), lane j gets V[kbase .. kbase+3][dbase + j] --
+//    four consecutive keys of one d, exactly the keys the S^T accumulator
+//    layout gives that lane's P;
+//  * LDS row pitches: K rows 272 B (8 consecutive rows of a 16-byte column
+//    hit disjoint banks), V rows 288 B (the 4 rows x 32 B of a transposed
+//    read hit disjoint banks);
+//  * the two 32-query blocks of a wave are staggered so that the matrix
+//    cores compute one block's S while the vector ALUs form the other
+//    block's P (phase list at the main loop);
+//  * online softmax in the log2 domain with a lazy rescale: the running max
+//    only moves (and O, l are rescaled) when a row's new max exceeds it by
+//    more than 8 (P stays <= 2^8); a wave-uniform branch, rarely taken;
 //  * GQA: the 4 wave tasks of a workgroup are (q block, head-in-group) pairs
 //    of one kv head, so a K/V tile in LDS serves every q head of the group.
+// This file is compiled with -fno-honor-nans (max without NaN quieting):
+// the softmax never produces NaN from finite inputs; -inf is still honoured.
 #include "../wm_internal.hpp"
 
 namespace wm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kKT = 64;   // keys per tile
-constexpr int kVP = kKT + 8;  // transposed-V row pitch (elements)
+constexpr int kKT = 64;                // keys per tile
+constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 template <int HD>
 struct Cfg {
-  static constexpr int KP = HD + 8;            // K row pitch in LDS (elements)
-  static constexpr int NDC = HD / 16;          // 16-wide d chunks (QK^T contraction)
-  static constexpr int NDB = HD / 32;          // 32-row d blocks (PV output)
-  static constexpr int CPR = HD / 8;           // 16-byte vectors per row
+  static constexpr int KP = HD + 8;     // K row pitch (elements)
+  static constexpr int VP = HD + 16;    // V row pitch (elements)
+  static constexpr int NDC = HD / 16;   // 16-wide d chunks (QK^T contraction)
+  static constexpr int NDB = HD / 32;   // 32-row d blocks (PV output)
+  static constexpr int CPR = HD / 8;    // 16-byte vectors per row
   static constexpr int K_ELEMS = kKT * KP;
-  static constexpr int V_ELEMS = HD * kVP;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
+  static constexpr int V_ELEMS = kKT * VP;
+  static constexpr int LDS_ELEMS = 2 * K_ELEMS + 3 * V_ELEMS;
 };
-
-// Position of key o (0..63) of a tile inside a transposed-V row: keys are
-// grouped so that the 8 keys a lane feeds to one PV MFMA are contiguous.
-__device__ __forceinline__ int vperm(int o) {
-  const int kb = o >> 5, r = o & 31;
-  return kb * 32 + (r >> 4) * 16 + ((r >> 2) & 1) * 8 + ((r >> 3) & 1) * 4 + (r & 3);
-}
 
 __device__ __forceinline__ float xhalf_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -67,15 +83,28 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int HD>
+// Row max of one 32-query block over a 64-key tile (both 32-key halves).
+__device__ __forceinline__ float tile_rowmax(const f32x16& a, const f32x16& b) {
+  float m0 = fmaxf(a[0], fmaxf(a[1], a[2]));
+  float m1 = fmaxf(b[0], fmaxf(b[1], b[2]));
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) {
+    m0 = fmaxf(m0, fmaxf(a[i], a[i + 1]));
+    m1 = fmaxf(m1, fmaxf(b[i], b[i + 1]));
+  }
+  return xhalf_max(fmaxf(m0, fmaxf(a[15], fmaxf(m1, b[15]))));
+}
+
+template <int HD, bool kSmallFt>
 __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParams p) {
   using C = Cfg<HD>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+  uint16_t* const kbuf0 = smem;
+  uint16_t* const vbuf0 = smem + 2 * C::K_ELEMS;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -97,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   const int ntiles = (nk + kKT - 1) / kKT;
   const int tps = (ntiles + p.nsplit - 1) / p.nsplit;
   const int t_begin = split * tps;
-  const int t_end = min(ntiles, t_begin + tps);
+  const int n_local = min(ntiles, t_begin + tps) - t_begin;  // >= 1 by construction
 
   const int task = wgi * kWaves + wave;
   const bool has_task = task < p.group * p.nqb;
@@ -109,81 +138,67 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   bf16x8 qreg[2][C::NDC];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int q = q0 + qb * 32 + l32;
-    const bool ok = has_task && q < p.nq;
-    const uint16_t* src = p.q + (((int64_t)b * p.nq + (ok ? q : 0)) * p.hq + h) * HD + hi * 8;
+    const int q = min(q0 + qb * 32 + l32, p.nq - 1);
+    const uint16_t* src = p.q + (((int64_t)b * p.nq + q) * p.hq + h) * HD + hi * 8;
 #pragma unroll
-    for (int dc = 0; dc < C::NDC; ++dc) {
-      uint4 v = ok ? *reinterpret_cast<const uint4*>(src + dc * 16) : make_uint4(0, 0, 0, 0);
-      qreg[qb][dc] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int dc = 0; dc < C::NDC; ++dc)
+      qreg[qb][dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src + dc * 16));
   }
 
   // ---- loader role: 4 consecutive keys x one 16-byte column chunk ----------
-  const int lkg = tid >> 4;      // key group 0..15 -> keys 4*lkg .. 4*lkg+3
-  const int lc = tid & 15;       // column chunk
-  const bool loader = lc < C::CPR;
-  const float inv_ft = 1.0f / (float)p.ft;
-  const int64_t ring_base = ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)p.ft * HD;
-  const int64_t slot_stride = (int64_t)p.hkv * p.ft * HD;
-  const int64_t chunk_base = ((int64_t)b * p.nq * p.hkv + g) * HD;
-  const int64_t chunk_stride = (int64_t)p.hkv * HD;
+  const int lkg = tid >> 4;  // key group 0..15 -> keys 4*lkg .. 4*lkg+3
+  const int lc = (tid & 15) % C::CPR;
+  const bool loader = (tid & 15) < C::CPR;
+  const int ft = p.ft;
+  const float inv_ft = 1.0f / (float)ft;
+  const uint16_t* const ring_k = p.pk + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD + lc * 8;
+  const uint16_t* const ring_v = p.pv + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD + lc * 8;
+  const uint32_t slot_stride = (uint32_t)p.hkv * ft * HD;  // elements; < 2^31 per rollout
+  const uint16_t* const chunk_k = p.kc + ((int64_t)b * p.nq * p.hkv + g) * HD + lc * 8;
+  const uint16_t* const chunk_v = p.vc + ((int64_t)b * p.nq * p.hkv + g) * HD + lc * 8;
+  const uint32_t chunk_stride = (uint32_t)p.hkv * HD;
 
-  uint4 kreg[4], vreg[4];
-  auto load_tile = [&](int tile) {
+  u32x4 kreg[4], vreg[4];
+  // Issue the loads of local tile u (keys clamped into range: always valid).
+  auto load_tile = [&](int u) {
+    const int j0 = (t_begin + u) * kKT + lkg * 4;
+    int s0 = (int)((float)j0 * inv_ft);
+    int r0 = j0 - s0 * ft;
+    s0 += (r0 >= ft) - (r0 < 0);
+    r0 = j0 - s0 * ft;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = tile * kKT + lkg * 4 + i;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (loader && j < nk) {
-        int64_t off;
-        const uint16_t *kb_, *vb_;
-        if (j < ring_keys) {
-          int s = (int)((float)j * inv_ft);
-          int r = j - s * p.ft;
-          if (r < 0) {
-            --s;
-            r += p.ft;
-          } else if (r >= p.ft) {
-            ++s;
-            r -= p.ft;
-          }
-          off = ring_base + s * slot_stride + (int64_t)r * HD;
-          kb_ = p.pk;
-          vb_ = p.pv;
-        } else {
-          off = chunk_base + (int64_t)(j - ring_keys) * chunk_stride;
-          kb_ = p.kc;
-          vb_ = p.vc;
+      int j = min(j0 + i, nk - 1);
+      int si, ri;
+      if constexpr (kSmallFt) {
+        si = (int)((float)j * inv_ft);
+        ri = j - si * ft;
+        si += (ri >= ft) - (ri < 0);
+        ri = j - si * ft;
+      } else {
+        // ft >= 4: at most one frame boundary inside the 4 keys
+        ri = r0 + i;
+        si = s0;
+        if (ri >= ft) {
+          ri -= ft;
+          ++si;
         }
-        off += lc * 8;
-        kv = *reinterpret_cast<const uint4*>(kb_ + off);
-        vv = *reinterpret_cast<const uint4*>(vb_ + off);
       }
-      kreg[i] = kv;
-      vreg[i] = vv;
+      const bool in_ring = j < ring_keys;
+      const uint32_t ro = (uint32_t)si * slot_stride + (uint32_t)ri * HD;
+      const uint32_t co = (uint32_t)(j - ring_keys) * chunk_stride;
+      const uint16_t* kp = in_ring ? ring_k + ro : chunk_k + co;
+      const uint16_t* vp = in_ring ? ring_v + ro : chunk_v + co;
+      kreg[i] = *reinterpret_cast<const u32x4*>(kp);
+      vreg[i] = *reinterpret_cast<const u32x4*>(vp);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](uint16_t* ks, uint16_t* vs) {
     if (!loader) return;
-    uint16_t* ks = smem + buf * C::STAGE;
-    uint16_t* vs = ks + C::K_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(ks + (lkg * 4 + i) * C::KP + lc * 8) = kreg[i];
-    const int pos = vperm(lkg * 4);
-    const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-    const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-    const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-    const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // d = lc*8 + 2w (low halves) and lc*8 + 2w + 1 (high halves)
-      const uint2 lo = make_uint2((v0[w] & 0xFFFFu) | (v1[w] << 16), (v2[w] & 0xFFFFu) | (v3[w] << 16));
-      const uint2 hi2 = make_uint2((v0[w] >> 16) | (v1[w] & 0xFFFF0000u),
-                                   (v2[w] >> 16) | (v3[w] & 0xFFFF0000u));
-      *reinterpret_cast<uint2*>(vs + (lc * 8 + 2 * w) * kVP + pos) = lo;
-      *reinterpret_cast<uint2*>(vs + (lc * 8 + 2 * w + 1) * kVP + pos) = hi2;
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(ks + (lkg * 4 + i) * C::KP + lc * 8) = kreg[i];
+      *reinterpret_cast<u32x4*>(vs + (lkg * 4 + i) * C::VP + lc * 8) = vreg[i];
     }
   };
 
@@ -195,105 +210,135 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[db][qb][i] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};  // running max (scaled, log2 domain)
+  float l_run[2] = {0.f, 0.f};              // running sum over this lane's keys
   const float sl2 = p.scale_log2e;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  if (t_begin < t_end) {
-    load_tile(t_begin);
-    store_tile(0);
-  }
-  __syncthreads();
+  // Transposed-read role: the lane's row and column inside its 16-lane group.
+  const int tr_l = lane & 15;
+  const int tr_off = (hi * 4 + (tr_l >> 2)) * C::VP + ((lane >> 4) & 1) * 16 + 4 * (tr_l & 3);
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const bool more = t + 1 < t_end;
-    if (more) load_tile(t + 1);
-
-    if (has_task) {
-      const uint16_t* ks = smem + buf * C::STAGE;
-      const uint16_t* vs = ks + C::K_ELEMS;
-      // S^T blocks: [kb][qb], keys kb*32.., queries qb*32..
-      f32x16 sacc[2][2];
+  // S^T of one 32-query block: S[kb], keys kb*32.., 16 fp32 per lane each.
+  auto qk = [&](const uint16_t* ks, int qb, f32x16 (&S)[2]) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * C::KP + hi * 8);
+      S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[qb][0], (f32x16){}, 0, 0, 0);
+    }
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[kb][qb][i] = 0.f;
+    for (int dc = 1; dc < C::NDC; ++dc) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int dc = 0; dc < C::NDC; ++dc) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * C::KP + dc * 16 + hi * 8);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[qb][dc], sacc[kb][qb], 0, 0, 0);
-        }
-      }
-      // Mask keys past the end (only the last tile can hold any).
-      const int kbase = t * kKT;
-      if (kbase + kKT > nk) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kbase + kb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-            if (key >= nk) {
-              sacc[kb][0][i] = -INFINITY;
-              sacc[kb][1][i] = -INFINITY;
-            }
-          }
-      }
-      // Online softmax (log2 domain), P^T fragments for the PV MFMA.
-      bf16x8 pfrag[2][4];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float mx = sacc[0][qb][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][qb][i]);
-        mx = xhalf_max(mx);
-        const float m_new = fmaxf(m_run[qb], mx * sl2);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          uint32_t pk[8];
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) {
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][i], sl2, -m_new));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][i + 1], sl2, -m_new));
-            rs += e0 + e1;
-            pk[i >> 1] = pack_bf16(e0, e1);
-          }
-          pfrag[qb][kb * 2 + 0] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-          pfrag[qb][kb * 2 + 1] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
-        }
-        l_run[qb] = l_run[qb] * alpha + rs;
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][qb][i] *= alpha;
-      }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * kVP + kc * 16 + hi * 8);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfrag[qb][kc], oacc[db][qb], 0, 0, 0);
-        }
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * C::KP + dc * 16 + hi * 8);
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[qb][dc], S[kb], 0, 0, 0);
       }
     }
+  };
+  // O^T[qb] += V^T P^T of one 32-query block; V^T fragments via transposed reads.
+  // MFMA kc covers keys kc*16..: lane half hi takes keys +4*hi+{0..3} and +8+4*hi+{0..3}.
+  auto pv = [&](const uint16_t* vs, int qb, const bf16x8 (&P)[4]) {
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const uint16_t* base = vs + tr_off + (kc * 16) * C::VP + db * 32;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * C::VP));
+        const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+        oacc[db][qb] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), P[kc], oacc[db][qb], 0, 0, 0);
+      }
+    }
+  };
+  // P^T fragments of one 32-key half of S: exp2(s*scale*log2e - m) in bf16, row sum.
+  auto softmax_half = [&](const f32x16& S, int qb, bf16x8& Pa, bf16x8& Pb) {
+    const float mneg = -m_run[qb];
+    uint32_t pk[8];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[i], sl2, mneg));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[i + 1], sl2, mneg));
+      const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+      l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[qb], false);
+      pk[i >> 1] = __builtin_bit_cast(uint32_t, pr);
+    }
+    Pa = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    Pb = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
+  };
+  // Mask keys >= nvalid of a tile (only the last tile of the key range).
+  auto mask_tail = [&](f32x16 (&S)[2], int nvalid) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+        if (key >= nvalid) S[kb][i] = -INFINITY;
+      }
+  };
+  // Lazy rescale of one query block (wave-uniform branch).
+  auto maybe_rescale = [&](int qb, float mxraw) {
+    const bool need = mxraw * sl2 > m_run[qb] + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = fmaxf(m_run[qb], mxraw * sl2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+      m_run[qb] = m_new;
+      l_run[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][qb][i] *= alpha;
+    }
+  };
 
-    if (more) store_tile(buf ^ 1);
+  const int nk_last = nk - (t_begin + n_local - 1) * kKT;  // valid keys in the last local tile
+  f32x16 S0[2], S1[2];
+  bf16x8 P0[4], P1[4];
+
+  // Prologue: K,V of tiles 0 and 1 in LDS; S of tile 0, block 0, and its row max.
+  load_tile(0);
+  store_tile(kbuf0, vbuf0);
+  load_tile(1);
+  store_tile(kbuf0 + C::K_ELEMS, vbuf0 + C::V_ELEMS);
+  __syncthreads();
+  qk(kbuf0, 0, S0);
+  float mx0 = tile_rowmax(S0[0], S0[1]);
+
+  // Per tile u (S0 = S(u, block 0) and its row max ready on entry):
+  //   A: S(u, block 1) on the matrix cores  || P(u, block 0) on the vector ALUs
+  //   B: O0 += V(u) P(u, block 0)             || first half of P(u, block 1)
+  //   C: S(u+1, block 0)                      || second half of P(u, block 1)
+  //   D: O1 += V(u) P(u, block 1)             || row max of S(u+1, block 0), LDS stores
+  // K is double-buffered (tile u+1 is read in C), V triple-buffered; the loads
+  // of tile u+2 are issued in A and land in LDS at the end of D.
+  for (int u = 0; u < n_local; ++u) {
+    const uint16_t* kcur = kbuf0 + (u & 1) * C::K_ELEMS;
+    const uint16_t* knext = kbuf0 + ((u + 1) & 1) * C::K_ELEMS;
+    const uint16_t* vcur = vbuf0 + (u % 3) * C::V_ELEMS;
+    const bool tail = u == n_local - 1 && nk_last < kKT;
+    if (tail) {
+      mask_tail(S0, nk_last);
+      mx0 = tile_rowmax(S0[0], S0[1]);
+    }
+    maybe_rescale(0, mx0);
+    // A
+    load_tile(u + 2);
+    qk(kcur, 1, S1);
+    softmax_half(S0[0], 0, P0[0], P0[1]);
+    softmax_half(S0[1], 0, P0[2], P0[3]);
+    if (tail) mask_tail(S1, nk_last);
+    maybe_rescale(1, tile_rowmax(S1[0], S1[1]));
+    // B
+    pv(vcur, 0, P0);
+    softmax_half(S1[0], 1, P1[0], P1[1]);
+    // C
+    qk(knext, 0, S0);
+    softmax_half(S1[1], 1, P1[2], P1[3]);
+    // D
+    pv(vcur, 1, P1);
+    mx0 = tile_rowmax(S0[0], S0[1]);
+    store_tile(kbuf0 + (u & 1) * C::K_ELEMS, vbuf0 + ((u + 2) % 3) * C::V_ELEMS);
     __syncthreads();
   }
 
@@ -321,7 +366,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
       // Partial result of this key range: O / l (fp32) plus (max, sum).
       const int64_t row = (((int64_t)split * p.nb + bi) * p.nq + q) * p.hq + h;
       float* dst = p.part_o + row * HD;
-      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      const float inv = 1.0f / l_tot;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -343,10 +388,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
 
 hipError_t launch_chunk_attn(const AttnParams& p, int head_dim, hipStream_t s) {
   const dim3 grid(p.nb * p.hkv * p.wg_per_bg * p.nsplit);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(chunk_attn_kernel<128>, grid, dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(chunk_attn_kernel<64>, grid, dim3(kThreads), 0, s, p);
+  const bool small = p.ft < 4;
+  if (head_dim == 128) {
+    if (small)
+      hipLaunchKernelGGL((chunk_attn_kernel<128, true>), grid, dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((chunk_attn_kernel<128, false>), grid, dim3(kThreads), 0, s, p);
+  } else {
+    if (small)
+      hipLaunchKernelGGL((chunk_attn_kernel<64, true>), grid, dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((chunk_attn_kernel<64, false>), grid, dim3(kThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 
