@@ -54,6 +54,9 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -87,6 +90,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Register-class pins (empty asm, no side effects): MFMA-only data (O, Q) in
+// AGPRs, data the vector ALUs touch (S) in VGPRs, so the allocator never
+// shuttles them across the rare rescale branch.
+template <typename T>
+__device__ __forceinline__ void pin_agpr(T& x) {
+  asm("" : "+a"(x));
+}
+template <typename T>
+__device__ __forceinline__ void pin_vgpr(T& x) {
+  asm("" : "+v"(x));
+}
+
 // Row max of one 32-query block over a 64-key tile (both 32-key halves).
 __device__ __forceinline__ float tile_rowmax(const f32x16& a, const f32x16& b) {
   float m0 = fmaxf(a[0], fmaxf(a[1], a[2]));
@@ -103,8 +118,8 @@ template <int HD, bool kSmallFt>
 __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParams p) {
   using C = Cfg<HD>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
-  uint16_t* const kbuf0 = smem;
-  uint16_t* const vbuf0 = smem + 2 * C::K_ELEMS;
+  lds_u16* const kbuf0 = (lds_u16*)smem;
+  lds_u16* const vbuf0 = kbuf0 + 2 * C::K_ELEMS;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -141,8 +156,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
     const int q = min(q0 + qb * 32 + l32, p.nq - 1);
     const uint16_t* src = p.q + (((int64_t)b * p.nq + q) * p.hq + h) * HD + hi * 8;
 #pragma unroll
-    for (int dc = 0; dc < C::NDC; ++dc)
+    for (int dc = 0; dc < C::NDC; ++dc) {
       qreg[qb][dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src + dc * 16));
+      pin_agpr(qreg[qb][dc]);
+    }
   }
 
   // ---- loader role: 4 consecutive keys x one 16-byte column chunk ----------
@@ -193,12 +210,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
       vreg[i] = *reinterpret_cast<const u32x4*>(vp);
     }
   };
-  auto store_tile = [&](uint16_t* ks, uint16_t* vs) {
+  auto store_tile = [&](lds_u16* ks, lds_u16* vs) {
     if (!loader) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(ks + (lkg * 4 + i) * C::KP + lc * 8) = kreg[i];
-      *reinterpret_cast<u32x4*>(vs + (lkg * 4 + i) * C::VP + lc * 8) = vreg[i];
+      *(lds_u32x4*)(ks + (lkg * 4 + i) * C::KP + lc * 8) = kreg[i];
+      *(lds_u32x4*)(vs + (lkg * 4 + i) * C::VP + lc * 8) = vreg[i];
     }
   };
 
@@ -218,34 +235,38 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   // Transposed-read role: the lane's row and column inside its 16-lane group.
   const int tr_l = lane & 15;
   const int tr_off = (hi * 4 + (tr_l >> 2)) * C::VP + ((lane >> 4) & 1) * 16 + 4 * (tr_l & 3);
+  const uint32_t tr_base = (uint32_t)(uintptr_t)(vbuf0 + tr_off);
 
   // S^T of one 32-query block: S[kb], keys kb*32.., 16 fp32 per lane each.
-  auto qk = [&](const uint16_t* ks, int qb, f32x16 (&S)[2]) {
+  auto qk = [&](const lds_u16* ks, int qb, f32x16 (&S)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * C::KP + hi * 8);
+      const bf16x8 kf = *(const lds_bf16x8*)(ks + (kb * 32 + l32) * C::KP + hi * 8);
       S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[qb][0], (f32x16){}, 0, 0, 0);
     }
 #pragma unroll
     for (int dc = 1; dc < C::NDC; ++dc) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * C::KP + dc * 16 + hi * 8);
+        const bf16x8 kf = *(const lds_bf16x8*)(ks + (kb * 32 + l32) * C::KP + dc * 16 + hi * 8);
         S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[qb][dc], S[kb], 0, 0, 0);
       }
     }
+    // pin_vgpr(S[0]);
+    // pin_vgpr(S[1]);
   };
   // O^T[qb] += V^T P^T of one 32-query block; V^T fragments via transposed reads.
   // MFMA kc covers keys kc*16..: lane half hi takes keys +4*hi+{0..3} and +8+4*hi+{0..3}.
-  auto pv = [&](const uint16_t* vs, int qb, const bf16x8 (&P)[4]) {
+  // trv is the 32-bit LDS byte address of this lane's first read in the tile;
+  // every other read is a compile-time byte offset from it.
+  auto pv = [&](uint32_t trv, int qb, const bf16x8 (&P)[4]) {
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const uint16_t* base = vs + tr_off + (kc * 16) * C::VP + db * 32;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * C::VP));
+        const uint32_t a = trv + 2 * ((kc * 16) * C::VP + db * 32);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a);
+        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(a + 2 * 8 * C::VP));
         const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
         oacc[db][qb] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), P[kc], oacc[db][qb], 0, 0, 0);
@@ -286,9 +307,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
       m_run[qb] = m_new;
       l_run[qb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
+      for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][qb][i] *= alpha;
+        pin_agpr(oacc[db][qb]);
+      }
     }
   };
 
@@ -313,9 +336,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   // K is double-buffered (tile u+1 is read in C), V triple-buffered; the loads
   // of tile u+2 are issued in A and land in LDS at the end of D.
   for (int u = 0; u < n_local; ++u) {
-    const uint16_t* kcur = kbuf0 + (u & 1) * C::K_ELEMS;
-    const uint16_t* knext = kbuf0 + ((u + 1) & 1) * C::K_ELEMS;
-    const uint16_t* vcur = vbuf0 + (u % 3) * C::V_ELEMS;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      pin_agpr(oacc[db][0]);
+      pin_agpr(oacc[db][1]);
+    }
+    const lds_u16* kcur = kbuf0 + (u & 1) * C::K_ELEMS;
+    const lds_u16* knext = kbuf0 + ((u + 1) & 1) * C::K_ELEMS;
+    uint32_t trv = tr_base + (uint32_t)((u % 3) * C::V_ELEMS * 2);
+    pin_vgpr(trv);  // opaque per-tile base: keeps base+const from being hoisted per read
     const bool tail = u == n_local - 1 && nk_last < kKT;
     if (tail) {
       mask_tail(S0, nk_last);
@@ -330,13 +359,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
     if (tail) mask_tail(S1, nk_last);
     maybe_rescale(1, tile_rowmax(S1[0], S1[1]));
     // B
-    pv(vcur, 0, P0);
+    pv(trv, 0, P0);
     softmax_half(S1[0], 1, P1[0], P1[1]);
     // C
     qk(knext, 0, S0);
     softmax_half(S1[1], 1, P1[2], P1[3]);
     // D
-    pv(vcur, 1, P1);
+    pv(trv, 1, P1);
     mx0 = tile_rowmax(S0[0], S0[1]);
     store_tile(kbuf0 + (u & 1) * C::K_ELEMS, vbuf0 + ((u + 2) % 3) * C::V_ELEMS);
     __syncthreads();
