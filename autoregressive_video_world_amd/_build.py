@@ -26,7 +26,7 @@ COMMON = [
 
 # Extra flags per source file (relative to csrc/).  The attention kernel is
 # built without NaN semantics so that max() needs no NaN-quieting instructions.
-PER_FILE = {os.path.join("kernels", "chunk_attn.hip"): ["-fno-honor-nans"]}
+PER_FILE = {os.path.join("kernels", "chunk_attn.hip"): ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def sources():

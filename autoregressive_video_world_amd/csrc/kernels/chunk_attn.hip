@@ -61,6 +61,7 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kKT = 64;                // keys per tile
+constexpr int kXcds = 8;               // MI355X: 8 accelerator complex dies
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 template <int HD>
@@ -128,7 +129,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   const int hi = lane >> 5;
 
   // ---- which (rollout, kv head, workgroup, split) -------------------------
-  int bid = blockIdx.x;
+  // Workgroups are dispatched round-robin over the 8 XCDs; remap so that each
+  // XCD gets a contiguous run of logical workgroups -- the q blocks of one kv
+  // head then stream the same K/V tiles through that XCD's L2.
+  int bid = (int)(blockIdx.x % kXcds) * p.per_xcd + (int)(blockIdx.x / kXcds);
+  if (bid >= p.n_wg) return;
   const int split = bid % p.nsplit;
   bid /= p.nsplit;
   const int wgi = bid % p.wg_per_bg;
@@ -415,8 +420,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
 
 }  // namespace
 
-hipError_t launch_chunk_attn(const AttnParams& p, int head_dim, hipStream_t s) {
-  const dim3 grid(p.nb * p.hkv * p.wg_per_bg * p.nsplit);
+hipError_t launch_chunk_attn(const AttnParams& p_in, int head_dim, hipStream_t s) {
+  AttnParams p = p_in;
+  p.n_wg = p.nb * p.hkv * p.wg_per_bg * p.nsplit;
+  p.per_xcd = (p.n_wg + kXcds - 1) / kXcds;
+  const dim3 grid(p.per_xcd * kXcds);
   const bool small = p.ft < 4;
   if (head_dim == 128) {
     if (small)

@@ -67,6 +67,8 @@ struct AttnParams {
   int32_t nqb;            // 64-query blocks per rollout
   int32_t wg_per_bg;      // workgroups per (rollout, kv head) per split
   int32_t nsplit;         // key-range splits (1 = none)
+  int32_t n_wg;           // logical workgroups (set by the launcher)
+  int32_t per_xcd;        // logical workgroups per XCD (set by the launcher)
   float scale_log2e;      // softmax scale * log2(e)
   int32_t nb;             // rollouts in this launch
   int32_t b_index[kAttnMaxB];
