@@ -13,28 +13,29 @@
 //
 // Design (one workgroup = 4 waves = 4 "wave tasks" that share one kv head):
 //  * a wave task is 64 queries of one q head: two 32-query blocks;
-//  * keys stream through LDS in 64-key tiles (K double-, V triple-buffered,
-//    one barrier per tile); tile loads are issued two tiles ahead and are
-//    branch-free: keys past the end are clamped to the last key and masked
-//    out of the softmax;
+//  * keys stream through LDS in 64-key tiles, K and V triple-buffered, with
+//    direct global->LDS loads (global_load_lds_dwordx4): no staging
+//    registers, no LDS store instructions.  A tile is stored column-major:
+//    16-byte column c of all 64 key rows is one contiguous 1 KB run (column
+//    pitch 1088 B), so one wave-wide DMA instruction fills one column with
+//    lane = key row, and every lane computes one row address per tile.  Keys
+//    past the end are clamped to the last key and masked out of the softmax;
 //  * S^T = K * Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T
-//    held in registers for the whole kernel): in the 32x32 accumulator
-//    layout each lane owns one query column and 16 keys, so the row max and
-//    row sum need one cross-half exchange (v_permlane32_swap), no tree;
+//    held in AGPRs for the whole kernel): in the 32x32 accumulator layout
+//    each lane owns one query column and 16 keys, so the row max and row sum
+//    need one cross-half exchange (v_permlane32_swap), no tree;
 //  * O^T += V^T * P^T on the same MFMA: P^T comes straight from the S^T
-//    accumulator (exp2, cvt_pk_bf16).  V stays in its natural [key][d] layout
-//    in LDS and the V^T operand is read with ds_read_b64_tr_b16: in each
-//    16-lane group, lane j receives element j%4 of the 8-byte chunks read by
-//    lanes j/4, j/4+4, j/4+8, j/4+12, so when lane L reads row kbase + L/4 at
-//    column dbase + 4*(L%4), lane j gets V[kbase .. kbase+3][dbase + j] --
-//    four consecutive keys of one d, exactly the keys the S^T accumulator
-//    layout gives that lane's P;
-//  * LDS row pitches: K rows 272 B (8 consecutive rows of a 16-byte column
-//    hit disjoint banks), V rows 288 B (the 4 rows x 32 B of a transposed
-//    read hit disjoint banks);
-//  * the two 32-query blocks of a wave are staggered so that the matrix
-//    cores compute one block's S while the vector ALUs form the other
-//    block's P (phase list at the main loop);
+//    accumulator (exp2, cvt_pk_bf16).  V^T operands are read with
+//    ds_read_b64_tr_b16: in each 16-lane group, lane j receives element j%4
+//    of the 8-byte chunks read by lanes j/4, j/4+4, j/4+8, j/4+12, so when
+//    lane L reads key row kbase + L/4 at dims dbase + 4*(L%4), lane j gets
+//    V[kbase .. kbase+3][dbase + j] -- four consecutive keys of one dim,
+//    exactly the keys the S^T accumulator layout gives that lane's P;
+//  * 32-key sub-tile pipeline: in sub-step j the matrix cores compute S of
+//    sub-tile j+1 and O += V P of sub-tile j-1 while the vector ALUs form P of
+//    sub-tile j.  Each K and V fragment read from LDS feeds both query
+//    blocks (LDS instruction count per tile halves compared with handling the
+//    blocks apart -- LDS issue, not bandwidth, is the scarce resource);
 //  * online softmax in the log2 domain with a lazy rescale: the running max
 //    only moves (and O, l are rescaled) when a row's new max exceeds it by
 //    more than 8 (P stays <= 2^8); a wave-uniform branch, rarely taken;
@@ -52,28 +53,25 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) uint16_t lds_u16;
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kKT = 64;                // keys per tile
 constexpr int kXcds = 8;               // MI355X: 8 accelerator complex dies
 constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr int kColPitch = kKT * 16 + 64;  // bytes per 16-byte column of a tile
 
 template <int HD>
 struct Cfg {
-  static constexpr int KP = HD + 8;     // K row pitch (elements)
-  static constexpr int VP = HD + 16;    // V row pitch (elements)
-  static constexpr int NDC = HD / 16;   // 16-wide d chunks (QK^T contraction)
-  static constexpr int NDB = HD / 32;   // 32-row d blocks (PV output)
-  static constexpr int CPR = HD / 8;    // 16-byte vectors per row
-  static constexpr int K_ELEMS = kKT * KP;
-  static constexpr int V_ELEMS = kKT * VP;
-  static constexpr int LDS_ELEMS = 2 * K_ELEMS + 3 * V_ELEMS;
+  static constexpr int NDC = HD / 16;             // 16-wide d chunks (QK^T contraction)
+  static constexpr int NDB = HD / 32;             // 32-row d blocks (PV output)
+  static constexpr int NCOL = HD / 8;             // 16-byte columns per key row
+  static constexpr int COLS_PER_WAVE = NCOL / kWaves;
+  static constexpr int TILE_BYTES = NCOL * kColPitch;
+  static constexpr int LDS_BYTES = 6 * TILE_BYTES;  // K x3, V x3
 };
 
 __device__ __forceinline__ float xhalf_max(float x) {
@@ -92,8 +90,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 }
 
 // Register-class pins (empty asm, no side effects): MFMA-only data (O, Q) in
-// AGPRs, data the vector ALUs touch (S) in VGPRs, so the allocator never
-// shuttles them across the rare rescale branch.
+// AGPRs, so the allocator never shuttles them across the rare rescale branch.
 template <typename T>
 __device__ __forceinline__ void pin_agpr(T& x) {
   asm("" : "+a"(x));
@@ -102,25 +99,48 @@ template <typename T>
 __device__ __forceinline__ void pin_vgpr(T& x) {
   asm("" : "+v"(x));
 }
+// Anchor: a side-effecting use that keeps a value's computation from being
+// sunk past this point (the compiler otherwise moves the softmax out of the
+// MFMA region, next to its first use, and nothing overlaps).
+template <typename T>
+__device__ __forceinline__ void anchor(const T& x) {
+  asm volatile("" ::"v"(x));
+}
 
-// Row max of one 32-query block over a 64-key tile (both 32-key halves).
-__device__ __forceinline__ float tile_rowmax(const f32x16& a, const f32x16& b) {
-  float m0 = fmaxf(a[0], fmaxf(a[1], a[2]));
-  float m1 = fmaxf(b[0], fmaxf(b[1], b[2]));
-#pragma unroll
-  for (int i = 3; i < 15; i += 2) {
-    m0 = fmaxf(m0, fmaxf(a[i], a[i + 1]));
-    m1 = fmaxf(m1, fmaxf(b[i], b[i + 1]));
-  }
-  return xhalf_max(fmaxf(m0, fmaxf(a[15], fmaxf(m1, b[15]))));
+// Wait until at most n of this wave's vector-memory operations are pending
+// (s_waitcnt vmcnt(n), other counters untouched).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Tile barrier: this wave's LDS reads done, at most n of its DMA transfers
+// still in flight, then s_barrier.  Written out instead of __syncthreads():
+// the workgroup release fence of the latter makes the compiler wait for every
+// outstanding DMA (vmcnt(0)), including the prefetch two tiles ahead.  The
+// asm carries a memory clobber, so no memory access moves across it.
+template <int n>
+__device__ __forceinline__ void tile_barrier() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4));  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
 }
 
 template <int HD, bool kSmallFt>
 __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParams p) {
   using C = Cfg<HD>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
-  lds_u16* const kbuf0 = (lds_u16*)smem;
-  lds_u16* const vbuf0 = kbuf0 + 2 * C::K_ELEMS;
+  // Six distinct LDS objects (not one array): the compiler can then prove that
+  // a read of one buffer never aliases a DMA still writing another, and does
+  // not stall the read on vmcnt(0).
+  __shared__ __attribute__((aligned(16))) uint8_t k0s[C::TILE_BYTES], k1s[C::TILE_BYTES], k2s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t v0s[C::TILE_BYTES], v1s[C::TILE_BYTES], v2s[C::TILE_BYTES];
+  lds_u8* const K0 = (lds_u8*)k0s;
+  lds_u8* const K1 = (lds_u8*)k1s;
+  lds_u8* const K2 = (lds_u8*)k2s;
+  lds_u8* const V0 = (lds_u8*)v0s;
+  lds_u8* const V1 = (lds_u8*)v1s;
+  lds_u8* const V2 = (lds_u8*)v2s;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -167,60 +187,35 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
     }
   }
 
-  // ---- loader role: 4 consecutive keys x one 16-byte column chunk ----------
-  const int lkg = tid >> 4;  // key group 0..15 -> keys 4*lkg .. 4*lkg+3
-  const int lc = (tid & 15) % C::CPR;
-  const bool loader = (tid & 15) < C::CPR;
+  // ---- tile loads: lane = key row, wave w fills columns w*CPW .. ------------
   const int ft = p.ft;
   const float inv_ft = 1.0f / (float)ft;
-  const uint16_t* const ring_k = p.pk + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD + lc * 8;
-  const uint16_t* const ring_v = p.pv + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD + lc * 8;
+  const uint16_t* const ring_k = p.pk + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD;
+  const uint16_t* const ring_v = p.pv + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD;
   const uint32_t slot_stride = (uint32_t)p.hkv * ft * HD;  // elements; < 2^31 per rollout
-  const uint16_t* const chunk_k = p.kc + ((int64_t)b * p.nq * p.hkv + g) * HD + lc * 8;
-  const uint16_t* const chunk_v = p.vc + ((int64_t)b * p.nq * p.hkv + g) * HD + lc * 8;
+  const uint16_t* const chunk_k = p.kc + ((int64_t)b * p.nq * p.hkv + g) * HD;
+  const uint16_t* const chunk_v = p.vc + ((int64_t)b * p.nq * p.hkv + g) * HD;
   const uint32_t chunk_stride = (uint32_t)p.hkv * HD;
+  const int col0 = wave * C::COLS_PER_WAVE;
 
-  u32x4 kreg[4], vreg[4];
-  // Issue the loads of local tile u (keys clamped into range: always valid).
-  auto load_tile = [&](int u) {
-    const int j0 = (t_begin + u) * kKT + lkg * 4;
-    int s0 = (int)((float)j0 * inv_ft);
-    int r0 = j0 - s0 * ft;
-    s0 += (r0 >= ft) - (r0 < 0);
-    r0 = j0 - s0 * ft;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int j = min(j0 + i, nk - 1);
-      int si, ri;
-      if constexpr (kSmallFt) {
-        si = (int)((float)j * inv_ft);
-        ri = j - si * ft;
-        si += (ri >= ft) - (ri < 0);
-        ri = j - si * ft;
-      } else {
-        // ft >= 4: at most one frame boundary inside the 4 keys
-        ri = r0 + i;
-        si = s0;
-        if (ri >= ft) {
-          ri -= ft;
-          ++si;
-        }
-      }
-      const bool in_ring = j < ring_keys;
-      const uint32_t ro = (uint32_t)si * slot_stride + (uint32_t)ri * HD;
-      const uint32_t co = (uint32_t)(j - ring_keys) * chunk_stride;
-      const uint16_t* kp = in_ring ? ring_k + ro : chunk_k + co;
-      const uint16_t* vp = in_ring ? ring_v + ro : chunk_v + co;
-      kreg[i] = *reinterpret_cast<const u32x4*>(kp);
-      vreg[i] = *reinterpret_cast<const u32x4*>(vp);
-    }
+  // Row pointers (K and V) of this lane's key row in local tile u.
+  auto row_ptrs = [&](int u, const uint16_t*& kp, const uint16_t*& vp) __attribute__((always_inline)) {
+    const int j = min((t_begin + u) * kKT + lane, nk - 1);
+    int s = (int)((float)j * inv_ft);
+    int r = j - s * ft;
+    s += (r >= ft) - (r < 0);
+    r = j - s * ft;
+    const bool in_ring = j < ring_keys;
+    const uint32_t ro = (uint32_t)s * slot_stride + (uint32_t)r * HD;
+    const uint32_t co = (uint32_t)(j - ring_keys) * chunk_stride;
+    kp = in_ring ? ring_k + ro : chunk_k + co;
+    vp = in_ring ? ring_v + ro : chunk_v + co;
   };
-  auto store_tile = [&](lds_u16* ks, lds_u16* vs) {
-    if (!loader) return;
+  auto dma_cols = [&](const uint16_t* rp, lds_u8* tile) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(lds_u32x4*)(ks + (lkg * 4 + i) * C::KP + lc * 8) = kreg[i];
-      *(lds_u32x4*)(vs + (lkg * 4 + i) * C::VP + lc * 8) = vreg[i];
+    for (int i = 0; i < C::COLS_PER_WAVE; ++i) {
+      const int c = col0 + i;
+      __builtin_amdgcn_global_load_lds(rp + c * 8, tile + c * kColPitch, 16, 0, 0);
     }
   };
 
@@ -237,144 +232,209 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   const float sl2 = p.scale_log2e;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // Transposed-read role: the lane's row and column inside its 16-lane group.
+  // LDS byte offsets of this lane's reads inside a tile.
+  //  K operand (A of S^T): key row kb*32 + l32, column 2*dc + hi.
+  const uint32_t k_off = (uint32_t)(hi * kColPitch + l32 * 16);
+  //  V^T operand: group lane L = lane & 15 reads key row +hi*4 + L/4, dims
+  //  dsub*16 + 4*(L&3) -> column dsub*2 + (L&3)/2, byte (L&1)*8 inside it.
   const int tr_l = lane & 15;
-  const int tr_off = (hi * 4 + (tr_l >> 2)) * C::VP + ((lane >> 4) & 1) * 16 + 4 * (tr_l & 3);
-  const uint32_t tr_base = (uint32_t)(uintptr_t)(vbuf0 + tr_off);
+  const uint32_t v_off = (uint32_t)((((lane >> 4) & 1) * 2 + ((tr_l & 3) >> 1)) * kColPitch +
+                                    (hi * 4 + (tr_l >> 2)) * 16 + (tr_l & 1) * 8);
 
-  // S^T of one 32-query block: S[kb], keys kb*32.., 16 fp32 per lane each.
-  auto qk = [&](const lds_u16* ks, int qb, f32x16 (&S)[2]) {
+  // S^T of a 32-key sub-tile (keys kb*32.. of the tile) for both query blocks:
+  // each K fragment read from LDS feeds two MFMAs.
+  auto qk = [&](const lds_u8* tile, int kb, f32x16 (&S)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 kf = *(const lds_bf16x8*)(ks + (kb * 32 + l32) * C::KP + hi * 8);
-      S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[qb][0], (f32x16){}, 0, 0, 0);
-    }
-#pragma unroll
-    for (int dc = 1; dc < C::NDC; ++dc) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *(const lds_bf16x8*)(ks + (kb * 32 + l32) * C::KP + dc * 16 + hi * 8);
-        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[qb][dc], S[kb], 0, 0, 0);
+    for (int dc = 0; dc < C::NDC; ++dc) {
+      const bf16x8 kf = *(const lds_bf16x8*)(tile + k_off + 2 * dc * kColPitch + kb * 512);
+      if (dc == 0) {
+        S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[0][0], (f32x16){}, 0, 0, 0);
+        S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[1][0], (f32x16){}, 0, 0, 0);
+      } else {
+        S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[0][dc], S[0], 0, 0, 0);
+        S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[1][dc], S[1], 0, 0, 0);
       }
     }
-    // pin_vgpr(S[0]);
-    // pin_vgpr(S[1]);
   };
-  // O^T[qb] += V^T P^T of one 32-query block; V^T fragments via transposed reads.
-  // MFMA kc covers keys kc*16..: lane half hi takes keys +4*hi+{0..3} and +8+4*hi+{0..3}.
-  // trv is the 32-bit LDS byte address of this lane's first read in the tile;
-  // every other read is a compile-time byte offset from it.
-  auto pv = [&](uint32_t trv, int qb, const bf16x8 (&P)[4]) {
+  // O^T += V^T P^T over a 32-key sub-tile, both query blocks; each V^T fragment
+  // (two transposed reads) feeds two MFMAs.  MFMA half h covers keys kb*32+16h..:
+  // lane half hi takes keys +4*hi+{0..3} and +8+4*hi+{0..3}.
+  auto pv = [&](const lds_u8* tile, int kb, const bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const uint32_t a = trv + 2 * ((kc * 16) * C::VP + db * 32);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a);
-        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(a + 2 * 8 * C::VP));
-        const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
-        oacc[db][qb] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), P[kc], oacc[db][qb], 0, 0, 0);
+      for (int half = 0; half < 2; ++half) {
+        const lds_u8* a = tile + v_off + db * 4 * kColPitch + (kb * 32 + half * 16) * 16;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
+        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * 16));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, (s16x8){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+        oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[0][half], oacc[db][0], 0, 0, 0);
+        oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[1][half], oacc[db][1], 0, 0, 0);
       }
     }
   };
-  // P^T fragments of one 32-key half of S: exp2(s*scale*log2e - m) in bf16, row sum.
-  auto softmax_half = [&](const f32x16& S, int qb, bf16x8& Pa, bf16x8& Pb) {
-    const float mneg = -m_run[qb];
-    uint32_t pk[8];
+  // P^T fragments of a sub-tile: exp2(s*scale*log2e - m) in bf16, and row sums.
+  auto softmax = [&](const f32x16 (&S)[2], bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[i], sl2, mneg));
-      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[i + 1], sl2, mneg));
-      const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
-      l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[qb], false);
-      pk[i >> 1] = __builtin_bit_cast(uint32_t, pr);
-    }
-    Pa = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    Pb = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
-  };
-  // Mask keys >= nvalid of a tile (only the last tile of the key range).
-  auto mask_tail = [&](f32x16 (&S)[2], int nvalid) {
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mneg = -m_run[qb];
+      uint32_t pk[8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-        if (key >= nvalid) S[kb][i] = -INFINITY;
+      for (int i = 0; i < 16; i += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][i], sl2, mneg));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][i + 1], sl2, mneg));
+        const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+        l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[qb], false);
+        pk[i >> 1] = __builtin_bit_cast(uint32_t, pr);
       }
+      P[qb][0] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+      P[qb][1] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
+    }
   };
-  // Lazy rescale of one query block (wave-uniform branch).
-  auto maybe_rescale = [&](int qb, float mxraw) {
-    const bool need = mxraw * sl2 > m_run[qb] + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_new = fmaxf(m_run[qb], mxraw * sl2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+  // Row max over a 32-key sub-tile (lane pair holds the 32 keys of a query).
+  auto sub_rowmax = [&](const f32x16& S) __attribute__((always_inline)) {
+    float m0 = fmaxf(S[0], fmaxf(S[1], S[2]));
+    float m1 = fmaxf(S[3], fmaxf(S[4], S[5]));
+#pragma unroll
+    for (int i = 6; i < 16; i += 4) {
+      m0 = fmaxf(m0, fmaxf(S[i], S[i + 1]));
+      m1 = fmaxf(m1, fmaxf(S[i + 2], S[i + 3]));
+    }
+    return xhalf_max(fmaxf(m0, m1));
+  };
+  // Mask keys >= nvalid of a sub-tile (only in the last tile of the key range).
+  auto mask_sub = [&](f32x16 (&S)[2], int nvalid) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = (i >> 2) * 8 + hi * 4 + (i & 3);
+      if (key >= nvalid) {
+        S[0][i] = -INFINITY;
+        S[1][i] = -INFINITY;
+      }
+    }
+  };
+  // Lazy rescale (wave-uniform, rarely taken).  The decision for sub-tile j is
+  // taken before its exponentials: the running max and sum move at once, but
+  // O is rescaled only after the still-pending P(j-1)*V -- formed against the
+  // old max -- has been accumulated (rescale_o at the end of the sub-step).
+  auto rescale_decide = [&](const float (&mx)[2], float (&alpha)[2]) __attribute__((always_inline)) {
+    const bool need = (mx[0] * sl2 > m_run[0] + kRescaleSlack) | (mx[1] * sl2 > m_run[1] + kRescaleSlack);
+    if (!__builtin_amdgcn_ballot_w64(need)) return false;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m_new = fmaxf(m_run[qb], mx[qb] * sl2);
+      alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
       m_run[qb] = m_new;
-      l_run[qb] *= alpha;
+      l_run[qb] *= alpha[qb];
+    }
+    return true;
+  };
+  auto rescale_o = [&](const float (&alpha)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][qb][i] *= alpha;
+        for (int i = 0; i < 16; ++i) oacc[db][qb][i] *= alpha[qb];
         pin_agpr(oacc[db][qb]);
       }
-    }
   };
+  // Sub-tile j of the local key range: mask what lies past the end, then the
+  // rescale decision on its row max.
+  const int nk_local = nk - t_begin * kKT;  // keys of this split's range (last tile may be partial)
+  auto prepare = [&](int j, f32x16 (&S)[2], float (&mx)[2], float (&alpha)[2]) __attribute__((always_inline)) {
+    const int nvalid = nk_local - j * 32;
+    if (nvalid < 32) {
+      mask_sub(S, nvalid);
+      mx[0] = sub_rowmax(S[0]);
+      mx[1] = sub_rowmax(S[1]);
+    }
+    return rescale_decide(mx, alpha);
+  };
+  f32x16 SA[2], SB[2];
+  bf16x8 PA[2][2], PB[2][2];
+  float mx[2];
+  const uint16_t *kp, *vp;
 
-  const int nk_last = nk - (t_begin + n_local - 1) * kKT;  // valid keys in the last local tile
-  f32x16 S0[2], S1[2];
-  bf16x8 P0[4], P1[4];
+  // Prologue: tiles 0 and 1 into LDS; S and row max of sub-tile 0.
+  row_ptrs(0, kp, vp);
+  dma_cols(kp, K0);
+  dma_cols(vp, V0);
+  row_ptrs(1, kp, vp);
+  dma_cols(kp, K1);
+  dma_cols(vp, V1);
+  tile_barrier<0>();
+  qk(K0, 0, SA);
+  mx[0] = sub_rowmax(SA[0]);
+  mx[1] = sub_rowmax(SA[1]);
 
-  // Prologue: K,V of tiles 0 and 1 in LDS; S of tile 0, block 0, and its row max.
-  load_tile(0);
-  store_tile(kbuf0, vbuf0);
-  load_tile(1);
-  store_tile(kbuf0 + C::K_ELEMS, vbuf0 + C::V_ELEMS);
-  __syncthreads();
-  qk(kbuf0, 0, S0);
-  float mx0 = tile_rowmax(S0[0], S0[1]);
-
-  // Per tile u (S0 = S(u, block 0) and its row max ready on entry):
-  //   A: S(u, block 1) on the matrix cores  || P(u, block 0) on the vector ALUs
-  //   B: O0 += V(u) P(u, block 0)             || first half of P(u, block 1)
-  //   C: S(u+1, block 0)                      || second half of P(u, block 1)
-  //   D: O1 += V(u) P(u, block 1)             || row max of S(u+1, block 0), LDS stores
-  // K is double-buffered (tile u+1 is read in C), V triple-buffered; the loads
-  // of tile u+2 are issued in A and land in LDS at the end of D.
-  for (int u = 0; u < n_local; ++u) {
+  // Two 32-key sub-steps per 64-key tile u.  Sub-step j computes
+  //   S(j+1) on the matrix cores (K fragments shared by both query blocks)
+  //   || P(j) = exp(S(j) - m) on the vector ALUs
+  //   || O += V P(j-1) on the matrix cores (V fragments shared likewise),
+  // then the row max of S(j+1).  K of tile u is read in sub-steps 2u-1 and
+  // 2u, V of tile u in 2u+1 and 2u+2.  The DMA of K(u+2) is issued at
+  // sub-step 2u into the buffer K(u-1) left, that of V(u+2) at 2u+1 into the
+  // buffer V(u-1) left; the one barrier per tile (end of sub-step 2u) is
+  // preceded by a wait that lets only the two newest DMA groups be in flight.
+  // Buffers rotate with period 3 (tile u uses K[u%3], V[u%3]); the caller
+  // passes them explicitly so every LDS access names a fixed object:
+  //   ku = K(u), kn = K(u+1), kf = K(u+2) (DMA target),
+  //   vu = V(u), vp_ = V(u-1) = V(u+2) (read in sub-step 2u, then DMA target).
+  auto tile_steps = [&](int u, bool first, lds_u8* ku, lds_u8* kn, lds_u8* kf, lds_u8* vu,
+                        lds_u8* vp_) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
       pin_agpr(oacc[db][0]);
       pin_agpr(oacc[db][1]);
     }
-    const lds_u16* kcur = kbuf0 + (u & 1) * C::K_ELEMS;
-    const lds_u16* knext = kbuf0 + ((u + 1) & 1) * C::K_ELEMS;
-    uint32_t trv = tr_base + (uint32_t)((u % 3) * C::V_ELEMS * 2);
-    pin_vgpr(trv);  // opaque per-tile base: keeps base+const from being hoisted per read
-    const bool tail = u == n_local - 1 && nk_last < kKT;
-    if (tail) {
-      mask_tail(S0, nk_last);
-      mx0 = tile_rowmax(S0[0], S0[1]);
-    }
-    maybe_rescale(0, mx0);
-    // A
-    load_tile(u + 2);
-    qk(kcur, 1, S1);
-    softmax_half(S0[0], 0, P0[0], P0[1]);
-    softmax_half(S0[1], 0, P0[2], P0[3]);
-    if (tail) mask_tail(S1, nk_last);
-    maybe_rescale(1, tile_rowmax(S1[0], S1[1]));
-    // B
-    pv(trv, 0, P0);
-    softmax_half(S1[0], 1, P1[0], P1[1]);
-    // C
-    qk(knext, 0, S0);
-    softmax_half(S1[1], 1, P1[2], P1[3]);
-    // D
-    pv(trv, 1, P1);
-    mx0 = tile_rowmax(S0[0], S0[1]);
-    store_tile(kbuf0 + (u & 1) * C::K_ELEMS, vbuf0 + ((u + 2) % 3) * C::V_ELEMS);
-    __syncthreads();
+    row_ptrs(u + 2, kp, vp);
+    dma_cols(kp, kf);
+    float alpha[2];
+    // sub-step 2u: S(2u) in SA, P(2u-1) in PB
+    bool resc = prepare(2 * u, SA, mx, alpha);
+    qk(ku, 1, SB);
+    softmax(SA, PA);
+    if (!first) pv(vp_, 1, PB);
+    anchor(PA[0][0]);
+    anchor(PA[0][1]);
+    anchor(PA[1][0]);
+    anchor(PA[1][1]);
+    mx[0] = sub_rowmax(SB[0]);
+    mx[1] = sub_rowmax(SB[1]);
+    if (resc) rescale_o(alpha);
+    tile_barrier<2 * C::COLS_PER_WAVE>();
+    // sub-step 2u+1: S(2u+1) in SB, P(2u) in PA
+    dma_cols(vp, vp_);
+    resc = prepare(2 * u + 1, SB, mx, alpha);
+    qk(kn, 0, SA);
+    softmax(SB, PB);
+    pv(vu, 0, PA);
+    anchor(PB[0][0]);
+    anchor(PB[0][1]);
+    anchor(PB[1][0]);
+    anchor(PB[1][1]);
+    mx[0] = sub_rowmax(SA[0]);
+    mx[1] = sub_rowmax(SA[1]);
+    if (resc) rescale_o(alpha);
+  };
+  tile_steps(0, true, K0, K1, K2, V0, V2);
+  int u = 1;
+  for (; u + 3 <= n_local; u += 3) {
+    tile_steps(u, false, K1, K2, K0, V1, V0);
+    tile_steps(u + 1, false, K2, K0, K1, V2, V1);
+    tile_steps(u + 2, false, K0, K1, K2, V0, V2);
   }
+  if (u < n_local) tile_steps(u++, false, K1, K2, K0, V1, V0);
+  if (u < n_local) tile_steps(u++, false, K2, K0, K1, V2, V1);
+  // P(2n-1): V of the last tile, keys 32..63.
+  switch ((n_local - 1) % 3) {
+    case 0: pv(V0, 1, PB); break;
+    case 1: pv(V1, 1, PB); break;
+    default: pv(V2, 1, PB); break;
+  }
+  // No DMA may still be writing this workgroup's LDS when it retires.
+  wait_vmcnt<0>();
 
   if (!has_task) return;
 

@@ -154,9 +154,12 @@ def test_rollout_parity(name):
     run_case(CASES[name])
 
 
-def test_rollout_parity_sharp_queries():
-    """Q scaled x8: a peaked softmax, where a dropped frame moves O by ~4e-2."""
-    run_case(CASES["mha_ft100_c2"], q_scale=8.0)
+@pytest.mark.parametrize("name", ["mha_ft100_c2", "gqa_ft70", "d64_ft50_c3", "batch3_staggered",
+                                  "chunk_gt_window"])
+def test_rollout_parity_sharp_queries(name):
+    """Q scaled x8: a peaked softmax (a dropped frame moves O by ~4e-2), and
+    row maxima that jump across key tiles, so the running-max rescale runs."""
+    run_case(CASES[name], q_scale=8.0)
 
 
 def test_rollout_parity_absolute_origins():
