@@ -166,13 +166,30 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   const int ntiles = (nk + kKT - 1) / kKT;
   const int tps = (ntiles + p.nsplit - 1) / p.nsplit;
   const int t_begin = split * tps;
-  const int n_local = min(ntiles, t_begin + tps) - t_begin;  // >= 1 by construction
+  const int n_local = min(ntiles, t_begin + tps) - t_begin;
 
   const int task = wgi * kWaves + wave;
   const bool has_task = task < p.group * p.nqb;
   const int qblk = has_task ? task / p.group : 0;
   const int h = g * p.group + (has_task ? task % p.group : 0);
   const int q0 = qblk * 64;
+
+  // A key-range split past the end of a short rollout's keys (ragged batch):
+  // record an empty partial (sum 0) and leave; the whole workgroup agrees.
+  if (n_local <= 0) {
+    if (has_task && lane < 32) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int q = q0 + qb * 32 + lane;
+        if (q < p.nq) {
+          const int64_t row = (((int64_t)split * p.nb + bi) * p.nq + q) * p.hq + h;
+          p.part_ml[row * 2 + 0] = -INFINITY;
+          p.part_ml[row * 2 + 1] = 0.f;
+        }
+      }
+    }
+    return;
+  }
 
   // ---- Q^T operands: lane (l32, hi) holds query q0+qb*32+l32, d = dc*16+hi*8.. --
   bf16x8 qreg[2][C::NDC];
@@ -478,6 +495,50 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   }
 }
 
+// Merge the key-range partials of a split launch: weights l_s * 2^(m_s - M)
+// over the splits with keys (log-sum-exp combine), one thread per 8 output
+// dims of one (rollout, query, head) row.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
+  constexpr int kCpr = HD / 8;
+  const int64_t rows = (int64_t)p.nb * p.nq * p.hq;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * kCpr) return;
+  const int c = (int)(idx % kCpr);
+  const int64_t row = idx / kCpr;
+  float M = -INFINITY;
+  for (int s = 0; s < p.nsplit; ++s) {
+    const float l = p.part_ml[(s * rows + row) * 2 + 1];
+    if (l > 0.f) M = fmaxf(M, p.part_ml[(s * rows + row) * 2 + 0]);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  for (int s = 0; s < p.nsplit; ++s) {
+    const float l = p.part_ml[(s * rows + row) * 2 + 1];
+    if (!(l > 0.f)) continue;
+    const float w = l * __builtin_amdgcn_exp2f(p.part_ml[(s * rows + row) * 2 + 0] - M);
+    wsum += w;
+    const float4* src = reinterpret_cast<const float4*>(p.part_o + (s * rows + row) * HD + c * 8);
+    const float4 a = src[0], b = src[1];
+    acc[0] += w * a.x;
+    acc[1] += w * a.y;
+    acc[2] += w * a.z;
+    acc[3] += w * a.w;
+    acc[4] += w * b.x;
+    acc[5] += w * b.y;
+    acc[6] += w * b.z;
+    acc[7] += w * b.w;
+  }
+  const float inv = 1.0f / wsum;
+  const int h = (int)(row % p.hq);
+  const int64_t qrow = row / p.hq;
+  const int q = (int)(qrow % p.nq);
+  const int bi = (int)(qrow / p.nq);
+  uint16_t* dst = p.out + (((int64_t)p.b_index[bi] * p.nq + q) * p.hq + h) * HD + c * 8;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv),
+                                              pack_bf16(acc[4] * inv, acc[5] * inv), pack_bf16(acc[6] * inv, acc[7] * inv));
+}
+
 }  // namespace
 
 hipError_t launch_chunk_attn(const AttnParams& p_in, int head_dim, hipStream_t s) {
@@ -496,6 +557,16 @@ hipError_t launch_chunk_attn(const AttnParams& p_in, int head_dim, hipStream_t s
       hipLaunchKernelGGL((chunk_attn_kernel<64, true>), grid, dim3(kThreads), 0, s, p);
     else
       hipLaunchKernelGGL((chunk_attn_kernel<64, false>), grid, dim3(kThreads), 0, s, p);
+  }
+  if (p.nsplit > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t threads = (int64_t)p.nb * p.nq * p.hq * (head_dim / 8);
+    const dim3 cgrid((unsigned)((threads + 255) / 256));
+    if (head_dim == 128)
+      hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

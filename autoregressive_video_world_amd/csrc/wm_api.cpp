@@ -321,11 +321,56 @@ wm_status do_append(wm_kvring* r, const wm_bf16* k_raw, const wm_bf16* v, int n_
   return WM_OK;
 }
 
+// Key-range split of an attention launch.  A launch of n_wg workgroups runs
+// in ceil(n_wg / CUs) rounds; splitting every key range s ways multiplies the
+// workgroups by s and divides their length by s, so time goes as
+// ceil(n_wg * s / CUs) / s.  Each split adds a partial row per query and head
+// (d fp32 written, then read by the combine: ~8d bytes at ~5 TB/s) against
+// 4*Nk*d flop of attention per row at ~1 PFLOP/s, i.e. ~400/Nk of the
+// attention time per split.  Each split keeps at least two 64-key tiles.
+constexpr int kCUs = 256;
+constexpr int kMaxSplit = 8;
+
+// WM_ATTN_SPLIT=n (1..8) overrides the choice (tuning and tests); read on
+// every call.
+int forced_split() {
+  const char* e = getenv("WM_ATTN_SPLIT");
+  if (!e) return 0;
+  const int v = atoi(e);
+  return v < 1 ? 0 : (v > kMaxSplit ? kMaxSplit : v);
+}
+
+int choose_split(int n_wg, int ntiles) {
+  const int forced = forced_split();
+  if (forced) return std::max(1, std::min(forced, ntiles));
+  const double per_split = 400.0 / (64.0 * ntiles);
+  int best = 1;
+  double best_cost = 1.0;
+  for (int s = 2; s <= kMaxSplit && ntiles >= 2 * s; ++s) {
+    const double rounds = std::ceil((double)n_wg * s / kCUs);
+    const double cost = rounds / s + per_split * s;
+    if (cost < best_cost - 1e-9) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+size_t split_ws_bytes(int nsplit, int nb, int nq, int hq, int hd) {
+  const size_t rows = (size_t)nsplit * nb * nq * hq;
+  return align_up(rows * hd * sizeof(float), 256) + rows * 2 * sizeof(float);
+}
+
+int wg_per_bg_of(const wm_kvring* r, int n_frames) {
+  const int group = r->desc.n_q_heads / r->desc.n_kv_heads;
+  const int nqb = (n_frames * r->ft + 63) / 64;
+  return (group * nqb + 3) / 4;
+}
+
 wm_status do_attn(const wm_kvring* r, const wm_bf16* q, const wm_bf16* kc, const wm_bf16* vc,
                   int n_frames, const uint8_t* active, float scale, wm_bf16* out, void* ws,
                   size_t ws_bytes, hipStream_t s) {
-  (void)ws;
-  (void)ws_bytes;
   const wm_kvring_desc& d = r->desc;
   wm::AttnParams p;
   memset(&p, 0, sizeof p);
@@ -342,22 +387,39 @@ wm_status do_attn(const wm_kvring* r, const wm_bf16* q, const wm_bf16* kc, const
   p.nq = n_frames * r->ft;
   p.ring_slots = r->R;
   p.nqb = (p.nq + 63) / 64;
-  p.wg_per_bg = (p.group * p.nqb + 3) / 4;
+  p.wg_per_bg = wg_per_bg_of(r, n_frames);
   p.nsplit = 1;
   const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)d.head_dim));
   p.scale_log2e = (float)((double)sc * 1.4426950408889634);
+  // Launch one group of rollouts, split when it pays and the workspace fits.
+  auto launch = [&](int max_ring) {
+    const int ntiles = ((max_ring + n_frames) * r->ft + 63) / 64;
+    int ns = choose_split(p.nb * p.hkv * p.wg_per_bg, ntiles);
+    while (ns > 1 && (!ws || split_ws_bytes(ns, p.nb, p.nq, p.hq, d.head_dim) > ws_bytes)) --ns;
+    p.nsplit = ns;
+    if (ns > 1) {
+      const size_t rows = (size_t)ns * p.nb * p.nq * p.hq;
+      p.part_o = static_cast<float*>(ws);
+      p.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
+                                           align_up(rows * d.head_dim * sizeof(float), 256));
+    }
+    return wm::launch_chunk_attn(p, d.head_dim, s);
+  };
+  int max_ring = 0;
   for (int b = 0; b < d.batch; ++b) {
     if (!is_active(active, b)) continue;
     p.b_index[p.nb] = b;
     p.n_ring[p.nb] = (int32_t)std::min<int64_t>(r->n_committed[b], r->R);
+    max_ring = std::max(max_ring, (int)p.n_ring[p.nb]);
     if (++p.nb == wm::kAttnMaxB) {
-      hipError_t e = wm::launch_chunk_attn(p, d.head_dim, s);
+      hipError_t e = launch(max_ring);
       if (e != hipSuccess) return hip_fail(e, "chunk_attn launch");
       p.nb = 0;
+      max_ring = 0;
     }
   }
   if (p.nb) {
-    hipError_t e = wm::launch_chunk_attn(p, d.head_dim, s);
+    hipError_t e = launch(max_ring);
     if (e != hipSuccess) return hip_fail(e, "chunk_attn launch");
   }
   return WM_OK;
@@ -505,9 +567,19 @@ wm_status wm_rope3d(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, int32_t
 }
 
 size_t wm_chunk_attn_workspace_bytes(const wm_kvring* ring, int32_t n_frames) {
-  (void)n_frames;
   if (check_ring(ring) != WM_OK) return 0;
-  return 0;
+  if (n_frames < 1 || n_frames > ring->desc.max_chunk) return 0;
+  // Largest workspace any launch group (1 .. min(B, rollouts per launch)
+  // rollouts, full window) would use.
+  const wm_kvring_desc& d = ring->desc;
+  const int ntiles = ((ring->R + n_frames) * ring->ft + 63) / 64;
+  const int nq = n_frames * ring->ft;
+  size_t best = 0;
+  for (int nb = 1; nb <= std::min(d.batch, wm::kAttnMaxB); ++nb) {
+    const int ns = choose_split(nb * d.n_kv_heads * wg_per_bg_of(ring, n_frames), ntiles);
+    if (ns > 1) best = std::max(best, split_ws_bytes(ns, nb, nq, d.n_q_heads, d.head_dim));
+  }
+  return best;
 }
 
 wm_status wm_chunk_attn(const wm_kvring* ring, const wm_bf16* q_rot, const wm_bf16* k_rot,

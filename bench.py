@@ -119,9 +119,13 @@ def main():
     q_rot = torch.empty_like(qs[0])
     k_rot = torch.empty_like(ks[0])
     stream = torch.cuda.current_stream()
+    # key-range split workspace (non-empty only where the grid is small)
+    ws_bytes = ring.workspace_bytes(C)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def step():
-        ring.rollout_step(qs, ks, vs, C, outs=outs, q_rot_scratch=q_rot, k_rot_scratch=k_rot)
+        ring.rollout_step(qs, ks, vs, C, outs=outs, q_rot_scratch=q_rot, k_rot_scratch=k_rot,
+                          workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -149,7 +153,7 @@ def main():
 
     ring.rope3d(qs[0], C, y=q_rot)
     ring.rope3d(ks[0], C, y=k_rot)
-    attn_mean, attn_med = timed(lambda: ring.chunk_attn(q_rot, k_rot, vs[0], C, out=outs[0]),
+    attn_mean, attn_med = timed(lambda: ring.chunk_attn(q_rot, k_rot, vs[0], C, out=outs[0], workspace=ws),
                                 args.kernel_reps)
     rope_q_mean, _ = timed(lambda: ring.rope3d(qs[0], C, y=q_rot), args.kernel_reps)
     rope_k_mean, _ = timed(lambda: ring.rope3d(ks[0], C, y=k_rot), args.kernel_reps)
@@ -188,7 +192,7 @@ def main():
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": prof_traffic,
                      "launch_ms_mean": round(attn_mean, 4), "launch_ms_median": round(attn_med, 4),
-                     "flops_per_launch": wl.attn_flops()},
+                     "flops_per_launch": wl.attn_flops(), "split_workspace_bytes": ws_bytes},
         "append": {"bound": "hbm", "achieved": round(app_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": round(app_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": app_bytes,
                    "launch_ms_mean": round(app_mean, 5), "launch_ms_median": round(app_med, 5)},

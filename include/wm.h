@@ -185,7 +185,11 @@ wm_status wm_rope3d(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, int32_t
  * softmax_scale <= 0 selects 1/sqrt(d).
  * workspace: optional device scratch for splitting long key ranges across
  * workgroups (more parallelism when B*Hq*Nq is small); NULL/0 = no split.
- * wm_chunk_attn_workspace_bytes() gives the size that enables the split.
+ * wm_chunk_attn_workspace_bytes() gives the size that enables the split.  The
+ * split count is chosen per launch from the workgroup count and key length;
+ * the environment variable WM_ATTN_SPLIT=n (1..8) overrides it (tuning,
+ * tests) and is also honoured by wm_chunk_attn_workspace_bytes().  A split
+ * that does not fit the given workspace is reduced until it does.
  * Errors: WM_E_ARG, WM_E_SHAPE, WM_E_STATE, WM_E_HIP. */
 wm_status wm_chunk_attn(const wm_kvring* ring, const wm_bf16* q_rot, const wm_bf16* k_rot,
                         const wm_bf16* v, int32_t n_frames, const uint8_t* active,

@@ -10,6 +10,7 @@ batches with inactive and staggered rollouts, and windows that wrap.
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -54,10 +55,44 @@ def check_pool(ring, oracles, used_slots):
                 assert np.all(pk[b, slot] == SENTINEL) and np.all(pv[b, slot] == SENTINEL), (b, slot)
 
 
-def run_case(wl, t0s=None, use_step=False, q_scale=1.0):
-    """Drive ``wl`` through the library and the oracle; compare everything."""
+class forced_split:
+    """Force the library's key-range split count (WM_ATTN_SPLIT) in a block."""
+
+    def __init__(self, n):
+        self.n = n
+
+    def __enter__(self):
+        self.old = os.environ.get("WM_ATTN_SPLIT")
+        if self.n:
+            os.environ["WM_ATTN_SPLIT"] = str(self.n)
+
+    def __exit__(self, *exc):
+        if self.old is None:
+            os.environ.pop("WM_ATTN_SPLIT", None)
+        else:
+            os.environ["WM_ATTN_SPLIT"] = self.old
+
+
+def workspace_for(ring, n_frames):
+    nbytes = ring.workspace_bytes(n_frames)
+    return torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
+
+
+def run_case(wl, t0s=None, use_step=False, q_scale=1.0, split=False):
+    """Drive ``wl`` through the library and the oracle; compare everything.
+
+    split=True hands the library a workspace, so launches with few
+    workgroups split their key ranges and combine partials."""
+    with forced_split(3 if split else 0):
+        return _run_case(wl, t0s, use_step, q_scale, split)
+
+
+def _run_case(wl, t0s, use_step, q_scale, split):
     src = Source(wl, q_scale=q_scale)
     ring, oracles = make_ring(wl, t0s)
+    ws = workspace_for(ring, wl.chunk) if split else None
+    if split:
+        assert ws is not None, "expected a key-range split"
     B, ft = wl.batch, wl.ft
     actions = [([("prefill", wl.prefill)] if wl.prefill else []) + [("gen", c) for c in wl.chunks()]
                for _ in range(B)]
@@ -91,7 +126,7 @@ def run_case(wl, t0s=None, use_step=False, q_scale=1.0):
                     outs_ref.append(refs)
                 if use_step:
                     outs, reps = ring.rollout_step([dev(x) for x in qs], [dev(x) for x in ks],
-                                                   [dev(x) for x in vs], n, active=active)
+                                                   [dev(x) for x in vs], n, active=active, workspace=ws)
                     for s in range(wl.n_denoise):
                         got = host(outs[s])
                         for b in bs:
@@ -102,7 +137,7 @@ def run_case(wl, t0s=None, use_step=False, q_scale=1.0):
                         qd, kd, vd = dev(qs[s]), dev(ks[s]), dev(vs[s])
                         q_rot = ring.rope3d(qd, n, active=active)
                         k_rot = ring.rope3d(kd, n, active=active)
-                        out = ring.chunk_attn(q_rot, k_rot, vd, n, active=active)
+                        out = ring.chunk_attn(q_rot, k_rot, vd, n, active=active, workspace=ws)
                         qr, kr, o = host(q_rot), host(k_rot), host(out)
                         for b in bs:
                             ref_q, ref_k, ref_o = outs_ref[s][b]
@@ -154,12 +189,20 @@ def test_rollout_parity(name):
     run_case(CASES[name])
 
 
+@pytest.mark.parametrize("name", [n for n in CASES if n != "tiny"])
+def test_rollout_parity_split_keys(name):
+    """Same rollouts with a workspace: key ranges split across workgroups."""
+    print("split case", name, flush=True)
+    run_case(CASES[name], split=True)
+
+
 @pytest.mark.parametrize("name", ["mha_ft100_c2", "gqa_ft70", "d64_ft50_c3", "batch3_staggered",
                                   "chunk_gt_window"])
 def test_rollout_parity_sharp_queries(name):
     """Q scaled x8: a peaked softmax (a dropped frame moves O by ~4e-2), and
     row maxima that jump across key tiles, so the running-max rescale runs."""
     run_case(CASES[name], q_scale=8.0)
+    run_case(CASES[name], q_scale=8.0, split=True)
 
 
 def test_rollout_parity_absolute_origins():
@@ -169,6 +212,8 @@ def test_rollout_parity_absolute_origins():
 @pytest.mark.parametrize("name", ["tiny", "batch3_staggered", "gqa_ft70"])
 def test_rollout_step_parity(name):
     run_case(CASES[name], use_step=True)
+    if name != "tiny":
+        run_case(CASES[name], use_step=True, split=True)
 
 
 def test_single_key_gives_value_bit_exact():
@@ -226,7 +271,8 @@ def test_full_size_steady_state_sampled(cfg):
     v_np = src.batch_chunk([n0], n, 0, "v")
     q_rot = ring.rope3d(dev(q_np), n)
     k_rot = ring.rope3d(dev(k_np), n)
-    out = host(ring.chunk_attn(q_rot, k_rot, dev(v_np), n))
+    ws = workspace_for(ring, n)
+    out = host(ring.chunk_attn(q_rot, k_rot, dev(v_np), n, workspace=ws))
     ref_q = ro.rope(q_np[0], n)
     ref_k = ro.rope(k_np[0], n)
     assert np.array_equal(host(q_rot)[0], ref_q)
