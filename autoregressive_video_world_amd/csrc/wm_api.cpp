@@ -84,7 +84,7 @@ bool bands_of(const wm_kvring_desc& d, Bands* b) {
 
 struct Layout {
   size_t k_off, v_off, tab_off;
-  size_t hcos, hsin, wcos, wsin;  // byte offsets of the tables
+  size_t hw;        // byte offset of the (cos, sin) table of the h then w band
   size_t tab_bytes, total;
 };
 
@@ -126,13 +126,10 @@ Layout layout_of(const wm_kvring_desc& d, const Bands& b) {
   L.k_off = 0;
   L.v_off = align_up(half, 256);
   L.tab_off = align_up(L.v_off + half, 256);
-  const size_t hb = (size_t)d.frame_h * (b.dh / 2) * sizeof(float);
-  const size_t wb = (size_t)d.frame_w * (b.dw / 2) * sizeof(float);
-  L.hcos = L.tab_off;
-  L.hsin = L.hcos + align_up(hb, 16);
-  L.wcos = L.hsin + align_up(hb, 16);
-  L.wsin = L.wcos + align_up(wb, 16);
-  L.tab_bytes = (L.wsin + align_up(wb, 16)) - L.tab_off;
+  const size_t entries = (size_t)d.frame_h * (b.dh / 2) + (size_t)d.frame_w * (b.dw / 2);
+  L.hw = L.tab_off;
+  // At least one entry: the kernels read entry 0 (unused) for t-band pairs.
+  L.tab_bytes = (entries ? entries : 1) * 2 * sizeof(double);
   L.total = align_up(L.tab_off + L.tab_bytes, 256);
   return L;
 }
@@ -172,20 +169,32 @@ bool is_active(const uint8_t* active, int b) { return !active || active[b] != 0;
 
 int64_t next_t(const wm_kvring* r, int b) { return r->t0[b] + r->n_committed[b]; }
 
-void t_row(const wm_kvring* r, int64_t t, float* c, float* s) {
+void t_row(const wm_kvring* r, int64_t t, float2* cs) {
   const int np = r->bands.dt / 2;
   for (int j = 0; j < np; ++j) {
     const double ang = (double)t * r->inv_t[j];
-    c[j] = (float)g_cos(ang);
-    s[j] = (float)g_sin(ang);
+    cs[j].x = (float)g_cos(ang);
+    cs[j].y = (float)g_sin(ang);
   }
 }
 
-void fill_tables_ptrs(const wm_kvring* r, wm::RopeParams* p) {
-  p->hcos = reinterpret_cast<const float*>(r->pool + r->L.hcos);
-  p->hsin = reinterpret_cast<const float*>(r->pool + r->L.hsin);
-  p->wcos = reinterpret_cast<const float*>(r->pool + r->L.wcos);
-  p->wsin = reinterpret_cast<const float*>(r->pool + r->L.wsin);
+// Multiplier and shift for wm::FastDiv (d >= 1, dividends below 2^31):
+// l = ceil(log2 d), mul = floor(2^32 (2^l - d) / d) + 1.
+wm::FastDiv fast_div_of(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint64_t mul = ((((uint64_t)1 << l) - d) << 32) / d + 1;
+  return wm::FastDiv{(uint32_t)mul, l};
+}
+
+void fill_tables_ptrs(const wm_kvring* r, wm::RopeParams* p, int n_heads) {
+  p->hw = reinterpret_cast<const double2*>(r->pool + r->L.hw);
+  p->w_base = r->desc.frame_h * (r->bands.dh / 2);
+  p->n_heads = n_heads;
+  p->lg_cpr = r->desc.head_dim == 128 ? 4 : 3;
+  p->row_vecs = r->ft * n_heads * (r->desc.head_dim / 8);
+  p->div_heads = fast_div_of((uint32_t)n_heads);
+  p->div_fw = fast_div_of((uint32_t)r->desc.frame_w);
   p->ft = r->ft;
   p->fw = r->desc.frame_w;
   p->d = r->desc.head_dim;
@@ -215,10 +224,9 @@ wm_status do_rope(const wm_kvring* r, const wm_bf16* x, wm_bf16* y, int n_heads,
                   const int64_t* t_first, const uint8_t* active, hipStream_t s) {
   wm::RopeParams p;
   memset(&p, 0, sizeof p);
-  fill_tables_ptrs(r, &p);
+  fill_tables_ptrs(r, &p, n_heads);
   p.x = x;
   p.y = y;
-  p.n_heads = n_heads;
   p.x_b_stride = (int64_t)n_frames * r->ft * n_heads * r->desc.head_dim;
   for (int b = 0; b < r->desc.batch; ++b) {
     if (!is_active(active, b)) continue;
@@ -228,7 +236,7 @@ wm_status do_rope(const wm_kvring* r, const wm_bf16* x, wm_bf16* y, int n_heads,
       row.b = b;
       row.j = j;
       row.slot = -1;
-      t_row(r, t0 + j, p.tcos[p.n_rows], p.tsin[p.n_rows]);
+      t_row(r, t0 + j, p.tcs[p.n_rows]);
       if (++p.n_rows == wm::kRopeRows) {
         hipError_t e = wm::launch_rope3d(p, s);
         if (e != hipSuccess) return hip_fail(e, "rope3d launch");
@@ -285,12 +293,11 @@ wm_status do_append(wm_kvring* r, const wm_bf16* k_raw, const wm_bf16* v, int n_
   if (!r->meta_only) {
     wm::RopeParams p;
     memset(&p, 0, sizeof p);
-    fill_tables_ptrs(r, &p);
+    fill_tables_ptrs(r, &p, r->desc.n_kv_heads);
     p.x = k_raw;
     p.vsrc = v;
     p.y = reinterpret_cast<uint16_t*>(r->pool + r->L.k_off);
     p.vdst = reinterpret_cast<uint16_t*>(r->pool + r->L.v_off);
-    p.n_heads = r->desc.n_kv_heads;
     p.x_b_stride = (int64_t)n_frames * r->ft * r->desc.n_kv_heads * r->desc.head_dim;
     for (int b = 0; b < B; ++b) {
       if (!is_active(active, b)) continue;
@@ -301,7 +308,7 @@ wm_status do_append(wm_kvring* r, const wm_bf16* k_raw, const wm_bf16* v, int n_
         row.b = b;
         row.j = j;
         row.slot = pl.slot;
-        t_row(r, reps[b].t[j], p.tcos[p.n_rows], p.tsin[p.n_rows]);
+        t_row(r, reps[b].t[j], p.tcs[p.n_rows]);
         if (++p.n_rows == wm::kRopeRows) {
           hipError_t e = wm::launch_kv_append(p, s);
           if (e != hipSuccess) return hip_fail(e, "kv_append launch");
@@ -473,18 +480,19 @@ wm_status wm_kvring_create(const wm_kvring_desc* desc, void* dev_pool, size_t po
   for (int j = 0; j < bands.dt / 2; ++j) r->inv_t.push_back(inv_freq(desc->rope_theta, j, bands.dt));
   if (!meta && L.tab_bytes) {
     std::vector<uint8_t> host(L.tab_bytes, 0);
-    auto fill = [&](size_t coff, size_t soff, int n_pos, int da) {
-      float* c = reinterpret_cast<float*>(host.data() + (coff - L.tab_off));
-      float* s = reinterpret_cast<float*>(host.data() + (soff - L.tab_off));
+    // fp64 copies of the fp32-rounded values (exact), so the kernels skip
+    // the widening.
+    double* cs = reinterpret_cast<double*>(host.data());
+    auto fill = [&](int n_pos, int da) {
       for (int pos = 0; pos < n_pos; ++pos)
         for (int j = 0; j < da / 2; ++j) {
           const double ang = (double)pos * inv_freq(desc->rope_theta, j, da);
-          c[pos * (da / 2) + j] = (float)g_cos(ang);
-          s[pos * (da / 2) + j] = (float)g_sin(ang);
+          *cs++ = (double)(float)g_cos(ang);
+          *cs++ = (double)(float)g_sin(ang);
         }
     };
-    fill(L.hcos, L.hsin, desc->frame_h, bands.dh);
-    fill(L.wcos, L.wsin, desc->frame_w, bands.dw);
+    fill(desc->frame_h, bands.dh);
+    fill(desc->frame_w, bands.dw);
     hipError_t e = hipMemcpy(r->pool + L.tab_off, host.data(), L.tab_bytes, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       delete r;

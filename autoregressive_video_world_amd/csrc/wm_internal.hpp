@@ -21,26 +21,36 @@ struct RopeRow {
   int32_t pad;
 };
 
+// n / d for n < 2^31 as (umulhi(n, mul) + n) >> shift (round-up multiplier
+// method of Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", 1994); the host computes mul and shift for d >= 1.
+struct FastDiv {
+  uint32_t mul;
+  uint32_t shift;
+};
+
 struct RopeParams {
   const uint16_t* x;      // rope: input chunk;  append: unrotated K of the chunk
   uint16_t* y;            // rope: output chunk; append: K half of the pool
   const uint16_t* vsrc;   // append only: V of the chunk
   uint16_t* vdst;         // append only: V half of the pool
-  const float* hcos;      // [frame_h][dh2]
-  const float* hsin;
-  const float* wcos;      // [frame_w][dw2]
-  const float* wsin;
+  const double2* hw;      // (cos, sin) table: [frame_h][dh2] of the h band, then
+                          // [frame_w][dw2] of the w band from entry w_base
   int64_t x_b_stride;     // elements per rollout in x / y (rope) or x / vsrc (append)
   int32_t n_heads;        // heads of x
   int32_t d;              // head dim
+  int32_t lg_cpr;         // log2(d / 8): 16-byte vectors per (token, head)
   int32_t ft;             // tokens per frame
   int32_t fw;             // frame width
+  int32_t row_vecs;       // 16-byte vectors per (rollout, frame) row = ft * n_heads * d / 8
   int32_t dt2, dh2, dw2;  // pairs per band
   int32_t ring_slots;     // S + W (append)
+  int32_t w_base;         // first entry of the w band in hw
   int32_t n_rows;
+  FastDiv div_heads;      // division by n_heads
+  FastDiv div_fw;         // division by frame width
   RopeRow rows[kRopeRows];
-  float tcos[kRopeRows][kMaxTPairs];
-  float tsin[kRopeRows][kMaxTPairs];
+  float2 tcs[kRopeRows][kMaxTPairs];  // (cos, sin) of the t band at each row's t
 };
 
 hipError_t launch_rope3d(const RopeParams& p, hipStream_t s);

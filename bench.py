@@ -40,8 +40,46 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, help="workload id (1-5), default 2")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4, help="q heads in the oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=12, help="q heads in the oracle sample")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one plain elementwise copy of this many MiB first (untimed), as the "
+                         "known-size reference for HBM byte counters")
     return ap.parse_args()
+
+
+def kernel_source_digest():
+    """sha256 over the attention kernel source, the internal header and the build flags."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "autoregressive_video_world_amd", "csrc")
+    for rel in ("kernels/chunk_attn.hip", "wm_internal.hpp"):
+        with open(os.path.join(csrc, rel), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(ROOT, "autoregressive_video_world_amd", "_build.py"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload_name):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, or None.
+
+    The summary records the source digest of the kernel it measured; a kernel
+    changed since then gets None (stale counters are not reported)."""
+    path = os.path.join(ROOT, "profiles", "chunk_attn_%s_hbm_traffic.md" % workload_name)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl, n_heads):
@@ -102,6 +140,15 @@ def main():
     def randn(*shape):
         return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
 
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 19  # bf16 elements
+        a = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.neg(a, out=b)  # reads and writes exactly n*2 bytes
+        torch.cuda.synchronize()
+        del a, b
+
     ring = wm.KVRing(1, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
                      wl.n_sink, wl.window, wl.chunk, device=dev)
     C, D, ft = wl.chunk, wl.n_denoise, wl.ft
@@ -140,24 +187,28 @@ def main():
     value = attn_flops_step * args.steps / elapsed / 1e12
 
     # ---- per-kernel timing with HIP events on the launch stream ------------
+    # `reps` launches back to back between one pair of events: the mean
+    # duration of a launch in a busy stream (an event pair around a single
+    # short launch would add the idle stream's dispatch latency, several us).
     def timed(fn, reps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        for a, b in evs:
-            a.record(stream)
-            fn()
-            b.record(stream)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        fn()
         torch.cuda.synchronize()
-        ts = sorted(a.elapsed_time(b) for a, b in evs)
-        return sum(ts) / len(ts), ts[len(ts) // 2]
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
 
     ring.rope3d(qs[0], C, y=q_rot)
     ring.rope3d(ks[0], C, y=k_rot)
-    attn_mean, attn_med = timed(lambda: ring.chunk_attn(q_rot, k_rot, vs[0], C, out=outs[0], workspace=ws),
-                                args.kernel_reps)
-    rope_q_mean, _ = timed(lambda: ring.rope3d(qs[0], C, y=q_rot), args.kernel_reps)
-    rope_k_mean, _ = timed(lambda: ring.rope3d(ks[0], C, y=k_rot), args.kernel_reps)
-    app_mean, app_med = timed(lambda: ring.append_evict(ks[-1], vs[-1], C), args.kernel_reps)
+    attn_mean = timed(lambda: ring.chunk_attn(q_rot, k_rot, vs[0], C, out=outs[0], workspace=ws),
+                      args.kernel_reps)
+    rope_q_mean = timed(lambda: ring.rope3d(qs[0], C, y=q_rot), args.kernel_reps)
+    rope_k_mean = timed(lambda: ring.rope3d(ks[0], C, y=k_rot), args.kernel_reps)
+    app_mean = timed(lambda: ring.append_evict(ks[-1], vs[-1], C), args.kernel_reps)
     torch.cuda.synchronize()
 
     attn_tflops = wl.attn_flops() / (attn_mean * 1e-3) / 1e12
@@ -165,7 +216,7 @@ def main():
     app_gbs = app_bytes / (app_mean * 1e-3) / 1e9
     rope_bytes = 2 * wl.nq * wl.head_dim * 2 * (wl.n_q_heads + wl.n_kv_heads)
     rope_gbs = rope_bytes / ((rope_q_mean + rope_k_mean) * 1e-3) / 1e9
-    prof_traffic = None  # filled from rocprofv3 --pmc runs (profiles/), not live
+    prof_traffic = profiled_traffic(wl.name)
 
     result = {
         "metric": METRIC,
@@ -191,11 +242,11 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "chunk_attn_kernel<128>",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": prof_traffic,
-                     "launch_ms_mean": round(attn_mean, 4), "launch_ms_median": round(attn_med, 4),
+                     "launch_ms_mean": round(attn_mean, 4),
                      "flops_per_launch": wl.attn_flops(), "split_workspace_bytes": ws_bytes},
         "append": {"bound": "hbm", "achieved": round(app_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": round(app_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": app_bytes,
-                   "launch_ms_mean": round(app_mean, 5), "launch_ms_median": round(app_med, 5)},
+                   "launch_ms_mean": round(app_mean, 5)},
         "rope": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
                  "launch_ms_mean_q": round(rope_q_mean, 5), "launch_ms_mean_k": round(rope_k_mean, 5)},

@@ -122,7 +122,9 @@ typedef struct {
  *   K half : bf16 [B][S+W][Hkv][Ft][d]   -- each (slot, kv head) one
  *                                           contiguous Ft x d block
  *   V half : bf16 [B][S+W][Hkv][Ft][d]   -- at offset K-half bytes
- *   tables : fp32 cos/sin rows of the h and w RoPE bands, 256-byte aligned
+ *   tables : (cos, sin) pairs of the h and w RoPE bands, [frame_h][d_h/2]
+ *            then [frame_w][d_w/2]: fp64 copies of fp32-rounded values,
+ *            256-byte aligned
  * Slot of frame f of a sequence: f if f < S, else S + (f - S) mod W.
  */
 size_t wm_kvring_pool_bytes(const wm_kvring_desc* desc);

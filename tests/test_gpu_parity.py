@@ -18,8 +18,9 @@ import torch
 
 import autoregressive_video_world_amd as wm
 from oracle.rollout import Rollout
+from oracle import bf16 as obf16
 from oracle import rope as orope
-from wm_synth import Source, Workload, WORKLOADS
+from wm_synth import Source, Workload, WORKLOADS, full_range_bits
 from gpu_util import assert_close, dev, host
 
 pytestmark = pytest.mark.gpu
@@ -228,6 +229,89 @@ def test_single_key_gives_value_bit_exact():
     # head h reads kv head h // 2
     for h in range(4):
         assert np.array_equal(out[0, 0, h], v_np[0, 0, h // 2])
+    ring.close()
+
+
+def plant_double_rounding_cases(x, t, h, w, rng, heads=(0,)):
+    """Overwrite (token, head, pair) entries of x (T, H, d) with (x0, 0) where
+    x0 * cos or x0 * sin (exact in fp64) rounds, in fp32, onto a bf16 midpoint
+    without being one: where rounding through fp32 (double rounding) can go
+    wrong.  Products are searched over all 128 bf16 significands at unit
+    exponent, then scaled by a random power of two (the fp32 rounding of a
+    normal product does not depend on the exponent), and over tiny x0 whose
+    products fall in the fp32 subnormal range.  Returns how many planted values
+    a naive fp64 -> fp32 -> bf16 path gets wrong."""
+    T, H, d = x.shape
+    cos, sin = orope.per_token_tables(t, h, w, d)
+    planted = np.zeros((T, d // 2), dtype=bool)
+    naive_wrong = 0
+
+    def plant(i, j, bits, c):
+        nonlocal naive_wrong
+        if planted[i, j]:
+            return
+        planted[i, j] = True
+        for hd in heads:
+            x[i, hd, 2 * j] = bits
+            x[i, hd, 2 * j + 1] = 0
+        prod = float(obf16.bits_to_f64(np.array([bits]))[0]) * c
+        fb = int(np.array([np.float32(prod)]).view(np.uint32)[0])
+        naive = ((fb + 0x7FFF + ((fb >> 16) & 1)) >> 16) & 0xFFFF
+        naive_wrong += int(naive != obf16.f64_to_bits(np.array([prod]))[0])
+
+    def search(x0_bits, tab):
+        prod = tab[:, :, None] * obf16.bits_to_f64(x0_bits)[None, None, :]
+        with np.errstate(all="ignore"):
+            f = prod.astype(np.float32)
+        fb = f.view(np.uint32)
+        return zip(*np.nonzero(((fb & 0xFFFF) == 0x8000) & (f.astype(np.float64) != prod)))
+
+    unit = (0x3F80 | np.arange(128)).astype(np.uint16)       # x0 in [1, 2)
+    tiny = np.concatenate([(e << 7) | np.arange(128) for e in range(1, 9)]).astype(np.uint16)
+    for tab in (cos, sin):
+        for i, j, m in search(unit, tab):
+            k = int(rng.integers(-20, 21))
+            sign = 0x8000 if rng.integers(2) else 0
+            plant(i, j, np.uint16(sign | ((127 + k) << 7) | (int(unit[m]) & 0x7F)), tab[i, j])
+        for n_hit, (i, j, m) in enumerate(search(tiny, tab)):
+            if n_hit % 5 == 0:
+                plant(i, j, tiny[m], tab[i, j])
+    return naive_wrong
+
+
+def test_rope_and_append_bit_exact_over_all_bf16_patterns():
+    """Random bit patterns over every exponent (subnormals, inf, NaN, extremes)
+    plus planted double-rounding cases, through wm_rope3d and the RoPE-fused
+    append at 1024 distinct absolute t (64 rollouts x 16 frames): both must
+    reproduce the oracle's rounding bit for bit."""
+    B, fh, fw, H, d, n = 64, 2, 2, 2, 128, 16
+    ft = fh * fw
+    rng = np.random.default_rng(140)
+    t0s = [int(v) for v in rng.integers(0, 1 << 20, size=B)]
+    x = full_range_bits(140, (B, n * ft, H, d))
+    v = full_range_bits(141, (B, n * ft, H, d))
+    want = np.empty_like(x)
+    naive_wrong = 0
+    for b in range(B):
+        t, h, w = orope.token_positions(n, fh, fw, t0s[b])
+        naive_wrong += plant_double_rounding_cases(x[b], t, h, w, rng, heads=(0, 1))
+        with np.errstate(invalid="ignore", over="ignore"):  # inf and NaN inputs
+            want[b] = orope.rotate(x[b], t, h, w)
+    assert naive_wrong >= 32, naive_wrong  # the hard case is really exercised
+
+    wl = W(140, batch=B, n_q_heads=H, n_kv_heads=H, frame_h=fh, frame_w=fw, chunk=n, n_sink=0,
+           window=n)
+    ring, _ = make_ring(wl, t0s=t0s)
+    got = host(ring.rope3d(dev(x), n))
+    bad = np.nonzero(got != want)
+    assert len(bad[0]) == 0, ("rope", len(bad[0]), list(zip(*[a[:5].tolist() for a in bad])))
+
+    ring.append_evict(dev(x), dev(v), n)
+    pk, pv = host(ring.pool_k()), host(ring.pool_v())
+    for b in range(B):
+        for j in range(n):  # frame j of the sequence sits in slot j
+            assert np.array_equal(pk[b, j], want[b, j * ft:(j + 1) * ft].transpose(1, 0, 2)), ("K", b, j)
+            assert np.array_equal(pv[b, j], v[b, j * ft:(j + 1) * ft].transpose(1, 0, 2)), ("V", b, j)
     ring.close()
 
 

@@ -150,3 +150,17 @@ class Source:
             if n0 is not None:
                 out[b] = self.chunk(b, n0, n_frames, s, kind)
         return out
+
+
+SPECIAL_BF16 = (0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F, 0xFF7F, 0x7F80, 0xFF80,
+                0x7FC0, 0xFFC1, 0x3F80, 0xBF80)
+
+
+def full_range_bits(seed, shape):
+    """Uniformly random bf16 bit patterns (every exponent, subnormals, inf, NaN),
+    with the special patterns above planted at the start."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0xB16]))
+    x = rng.integers(0, 1 << 16, size=shape, dtype=np.uint32).astype(np.uint16)
+    flat = x.reshape(-1)
+    flat[:len(SPECIAL_BF16)] = SPECIAL_BF16
+    return x
