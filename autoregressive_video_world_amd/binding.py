@@ -122,8 +122,7 @@ def _active(active, batch):
 
 def _report_dict(r):
     n, ne = r.n_written, r.n_evicted
-    return {"written": [(r.frame[i], r.slot[i], r.t[i]) for i in range(n)],
-            "evicted": [r.evicted[i] for i in range(ne)]}
+    return {"written": list(zip(r.frame[:n], r.slot[:n], r.t[:n])), "evicted": r.evicted[:ne]}
 
 
 class KVRing:
@@ -138,6 +137,9 @@ class KVRing:
         self.fh, self.fw, self.ft = frame_h, frame_w, frame_h * frame_w
         self.n_sink, self.window, self.max_chunk = n_sink, window, max_chunk
         self.slots = n_sink + window
+        # report buffer reused by every append (no per-call ctypes allocation)
+        self._reps = (AppendReport * batch)()
+        self._reps_ptr = ctypes.c_void_p(ctypes.addressof(self._reps))
         self.pool_bytes = lib().wm_kvring_pool_bytes(ctypes.byref(self.desc))
         if self.pool_bytes == 0:
             raise WMError(2, "invalid ring descriptor")
@@ -224,16 +226,14 @@ class KVRing:
 
     def append_evict(self, k_raw, v, n_frames, active=None, stream=None):
         nk_el = self.tokens(n_frames, self.hkv)
-        reps = (AppendReport * self.batch)()
         act_arr, act = _active(active, self.batch)
         if self.pool is None:                      # metadata-only ring: no device data
             kp = vp = None
         else:
             kp, vp = _ptr(k_raw, "k_raw", numel=nk_el), _ptr(v, "v", numel=nk_el)
-        _check(lib().wm_kvring_append_evict(self._h, kp, vp, n_frames, act,
-                                            ctypes.cast(reps, ctypes.c_void_p),
+        _check(lib().wm_kvring_append_evict(self._h, kp, vp, n_frames, act, self._reps_ptr,
                                             None if self.pool is None else _stream(stream)))
-        return [_report_dict(r) for r in reps]
+        return [_report_dict(r) for r in self._reps]
 
     def rollout_step(self, qs, ks, vs, n_frames, outs=None, active=None, q_rot_scratch=None,
                      k_rot_scratch=None, workspace=None, stream=None):
@@ -249,13 +249,11 @@ class KVRing:
         arr = lambda ts, what, n: (ctypes.c_void_p * D)(*[_ptr(t, what, numel=n) for t in ts])
         qa, ka, va = arr(qs, "q", nq_el), arr(ks, "k", nk_el), arr(vs, "v", nk_el)
         oa = arr(outs, "out", nq_el)
-        reps = (AppendReport * self.batch)()
         act_arr, act = _active(active, self.batch)
         ws = _ptr(workspace, "workspace", dtype=torch.uint8)
         ws_bytes = 0 if workspace is None else workspace.numel()
         _check(lib().wm_rollout_step(self._h, D, qa, ka, va, n_frames, act,
                                      _ptr(q_rot_scratch, "q_rot_scratch", numel=nq_el),
                                      _ptr(k_rot_scratch, "k_rot_scratch", numel=nk_el),
-                                     oa, ws, ws_bytes, ctypes.cast(reps, ctypes.c_void_p),
-                                     _stream(stream)))
-        return outs, [_report_dict(r) for r in reps]
+                                     oa, ws, ws_bytes, self._reps_ptr, _stream(stream)))
+        return outs, [_report_dict(r) for r in self._reps]

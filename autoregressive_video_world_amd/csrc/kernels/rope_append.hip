@@ -1,9 +1,10 @@
 // 3D-RoPE of a chunk and the RoPE-fused KV append (gfx950).
 //
 // Both kernels are HBM-bound streams over 16-byte vectors (8 bf16 = 4
-// rotation pairs of one (token, head) row).  Each thread owns kVecs vectors,
-// 256 vectors apart, and issues all of its loads before any arithmetic, so a
-// wave keeps 4 (rope) or 8 (append) 16-byte loads in flight.
+// rotation pairs of one (token, head) row).  Each thread owns the same
+// 16-byte slot of one token in kHeads heads and issues all of its loads
+// before any arithmetic, so a wave keeps 4 (rope) or 8 (append) 16-byte loads
+// in flight per lane.
 //
 // Rotation, exactly: a bf16 value times an fp32 table entry is exact in fp64,
 // so y0 = x0*c - x1*s and y1 = x0*s + x1*c are each rounded once to fp64 (one
@@ -25,7 +26,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int kVecs = 4;  // 16-byte vectors per thread
+constexpr int kHeads = 4;  // heads per thread
 
 __device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv d) {
   return (__umulhi(n, d.mul) + n) >> d.shift;
@@ -91,150 +92,120 @@ __device__ __forceinline__ u32x4 rotate_vec(u32x4 x, const double (&c)[4], const
   return o;
 }
 
-// Per-thread constants of its four pairs.  A pair's band is fixed by its index
-// within the head dim, which is the same for all of a thread's vectors (they
-// are 256 apart), so the t-band entries are loaded once.  Every pair reads one
-// pool-table entry (byte offset sel(pair) + off(pair) with sel the token's h or
-// w row); t-band pairs read a valid but unused entry and blend it out with
-// c = e*0 + c_t (e finite, and the t rows hold no -0, so this is exactly c_t),
-// h/w pairs with c = e*1 + (-0) (exactly e).  The blend keeps the table loads
-// unconditional (no branch per pair).
-struct PairBands {
-  bool in_h[4];
-  uint32_t off16[4];    // byte offset of the pair's entry within its row
-  double keep[4];       // 1 for h/w pairs, 0 for t pairs
-  double tc[4], ts[4];  // t-band (cos, sin), or -0 for h/w pairs
-};
-
-__device__ __forceinline__ void pair_tables(const RopeParams& p, const PairBands& pb,
-                                            uint32_t hrow16, uint32_t wrow16, double (&c)[4],
-                                            double (&s)[4]) {
-  const char* base = reinterpret_cast<const char*>(p.hw);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t off = (pb.in_h[k] ? hrow16 : wrow16) + pb.off16[k];
-    const double2 e = *reinterpret_cast<const double2*>(base + off);
-    c[k] = __builtin_fma(e.x, pb.keep[k], pb.tc[k]);
-    s[k] = __builtin_fma(e.y, pb.keep[k], pb.ts[k]);
+// (cos, sin) of pair pr at the token (hpos, wpos): the t band from the row's
+// kernel-argument values, the h and w bands from the pool table.
+__device__ __forceinline__ void pair_entry(const RopeParams& p, int row, int pr, uint32_t hpos,
+                                           uint32_t wpos, double& c, double& s) {
+  if (pr < p.dt2) {
+    c = p.tcs[row][pr].x;
+    s = p.tcs[row][pr].y;
+  } else {
+    const uint32_t e = pr < p.dt2 + p.dh2
+                           ? hpos * p.dh2 + (pr - p.dt2)
+                           : p.w_base + wpos * p.dw2 + (pr - p.dt2 - p.dh2);
+    c = p.hw[e].x;
+    s = p.hw[e].y;
   }
 }
 
-// grid: x = ceil(row_vecs / (256 * kVecs)), y = row of p.rows
-template <bool kAppend>
-__global__ __launch_bounds__(kThreads, 4) void rope_rows_kernel(const RopeParams p) {
+// grid: x = ceil(ft / tokens per block), y = row of p.rows, z = ceil(n_heads / kHeads).
+// Thread = (token, 16-byte slot c8 of the head dim); it handles kHeads heads of
+// that token, so its four pairs' table entries and its token's position are
+// looked up once.  A wave covers 64 / (d/8) consecutive tokens: each head's
+// rows are 256-byte (d = 128) runs in the chunk tensor and, in the pool
+// ([head][token][d]), one contiguous run.
+template <bool kAppend, int kLgCpr>
+__global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p) {
+  constexpr int kCpr = 1 << kLgCpr;  // 16-byte vectors per (token, head)
+  constexpr int kTpb = kThreads / kCpr;
   const int row = blockIdx.y;
+  const uint32_t c8 = threadIdx.x & (kCpr - 1);
+  const uint32_t tok = blockIdx.x * kTpb + (threadIdx.x >> kLgCpr);
+  if (tok >= (uint32_t)p.ft) return;
+  const int h0 = blockIdx.z * kHeads;
+  const int nh = min(kHeads, p.n_heads - h0);
   const int rb = p.rows[row].b;
   const int rj = p.rows[row].j;
-  const uint32_t nvec = (uint32_t)p.row_vecs;
-  // A row's vectors are contiguous in the chunk tensor ([token][head][d]);
-  // 32-bit byte offsets (a row holds below 2^28 vectors).
-  const int64_t row_base = (int64_t)rb * p.x_b_stride + (int64_t)rj * nvec * 8;
-  const char* xs = reinterpret_cast<const char*>(p.x + row_base);
-  const char* vs = reinterpret_cast<const char*>(p.vsrc + row_base);
+  const uint32_t head_bytes = (uint32_t)kCpr * 16u;
 
-  // Loads first (indices clamped into the row; stores are predicated).
-  uint32_t vi[kVecs];
-  u32x4 kx[kVecs], vx[kVecs];
+  // Loads first (heads past the last are clamped; their stores are skipped).
+  // A frame of the chunk holds below 2^28 elements: 32-bit byte offsets.
+  const int64_t row_base = (int64_t)rb * p.x_b_stride + (int64_t)rj * p.ft * p.n_heads * (kCpr * 8);
+  const uint32_t src_off = ((tok * (uint32_t)p.n_heads + h0) * kCpr + c8) * 16u;
+  const char* xs = reinterpret_cast<const char*>(p.x + row_base) + src_off;
+  const char* vs = reinterpret_cast<const char*>(p.vsrc + row_base) + src_off;
+  u32x4 kx[kHeads], vx[kHeads];
 #pragma unroll
-  for (int u = 0; u < kVecs; ++u) {
-    vi[u] = (blockIdx.x * kVecs + u) * kThreads + threadIdx.x;
-    const uint32_t off = (vi[u] < nvec ? vi[u] : nvec - 1) * 16u;
-    kx[u] = *reinterpret_cast<const u32x4*>(xs + off);
-    if constexpr (kAppend) vx[u] = *reinterpret_cast<const u32x4*>(vs + off);
+  for (int g = 0; g < kHeads; ++g) {
+    const uint32_t off = (uint32_t)(g < nh ? g : nh - 1) * head_bytes;
+    kx[g] = *reinterpret_cast<const u32x4*>(xs + off);
+    if constexpr (kAppend) vx[g] = *reinterpret_cast<const u32x4*>(vs + off);
   }
 
-  const uint32_t c8 = threadIdx.x & ((1u << p.lg_cpr) - 1);
-  const int ht = p.dt2 + p.dh2;
-  PairBands pb;
+  const uint32_t hpos = fast_div(tok, p.div_fw);
+  const uint32_t wpos = tok - hpos * p.fw;
+  double c[4], s[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int pr = (int)c8 * 4 + k;
-    const bool in_t = pr < p.dt2;
-    pb.in_h[k] = pr < ht;
-    pb.off16[k] = in_t ? 0u : 16u * (uint32_t)(pr < ht ? pr - p.dt2 : pr - ht);
-    pb.keep[k] = in_t ? 0.0 : 1.0;
-    const float2 t = p.tcs[row][in_t ? pr : 0];
-    pb.tc[k] = in_t ? (double)t.x : -0.0;
-    pb.ts[k] = in_t ? (double)t.y : -0.0;
-  }
+  for (int k = 0; k < 4; ++k) pair_entry(p, row, (int)c8 * 4 + k, hpos, wpos, c[k], s[k]);
 
-  // Pool destination of a (head, token): per-row slot block + 32-bit offset.
-  uint16_t* kdst = nullptr;
-  uint16_t* vdst = nullptr;
+  // Destinations: the chunk layout (rope) or the slot's [head][token][d] block.
+  char* kout;
+  char* vout = nullptr;
+  uint32_t dst_off, dst_head;
   if constexpr (kAppend) {
     const int64_t slot_base =
-        ((int64_t)rb * p.ring_slots + p.rows[row].slot) * p.n_heads * p.ft * p.d;
-    kdst = p.y + slot_base;
-    vdst = p.vdst + slot_base;
+        ((int64_t)rb * p.ring_slots + p.rows[row].slot) * p.n_heads * p.ft * (kCpr * 8);
+    kout = reinterpret_cast<char*>(p.y + slot_base);
+    vout = reinterpret_cast<char*>(p.vdst + slot_base);
+    dst_head = (uint32_t)p.ft * head_bytes;
+    dst_off = (uint32_t)h0 * dst_head + (tok * kCpr + c8) * 16u;
+  } else {
+    kout = reinterpret_cast<char*>(p.y + row_base);
+    dst_head = head_bytes;
+    dst_off = src_off;
   }
-  const uint32_t head_stride16 = (uint32_t)p.ft * p.d * 2u;
-
-  // Token decomposition of vector vi: table rows and pool offset.
-  struct Where {
-    uint32_t hrow16, wrow16, dst16;
-  };
-  auto where = [&](uint32_t v) __attribute__((always_inline)) {
-    const uint32_t th = v >> p.lg_cpr;  // token * n_heads + head
-    const uint32_t tok = fast_div(th, p.div_heads);
-    const uint32_t head = th - tok * p.n_heads;
-    const uint32_t hpos = fast_div(tok, p.div_fw);
-    const uint32_t wpos = tok - hpos * p.fw;
-    Where r;
-    r.hrow16 = hpos * (uint32_t)p.dh2 * 16u;
-    r.wrow16 = (wpos * (uint32_t)p.dw2 + (uint32_t)p.w_base) * 16u;
-    r.dst16 = kAppend ? head * head_stride16 + (tok * (uint32_t)p.d + c8 * 8u) * 2u : v * 16u;
-    return r;
-  };
-  char* kout = kAppend ? reinterpret_cast<char*>(kdst) : reinterpret_cast<char*>(p.y + row_base);
 
   uint32_t fix_mask = 0;
 #pragma unroll
-  for (int u = 0; u < kVecs; ++u) {
-    const Where at = where(vi[u]);
-    double c[4], s[4];
-    pair_tables(p, pb, at.hrow16, at.wrow16, c, s);
+  for (int g = 0; g < kHeads; ++g) {
     FixDetect det;
-    const u32x4 o = rotate_vec<false>(kx[u], c, s, det);
-    if (vi[u] >= nvec) continue;
-    fix_mask |= (uint32_t)det.needed() << u;
-    *reinterpret_cast<u32x4*>(kout + at.dst16) = o;
-    if constexpr (kAppend) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(vdst) + at.dst16) = vx[u];
+    const u32x4 o = rotate_vec<false>(kx[g], c, s, det);
+    if (g >= nh) continue;
+    fix_mask |= (uint32_t)det.needed() << g;
+    *reinterpret_cast<u32x4*>(kout + dst_off + g * dst_head) = o;
+    if constexpr (kAppend) *reinterpret_cast<u32x4*>(vout + dst_off + g * dst_head) = vx[g];
   }
 
   // Rare second pass: exact recomputation of flagged vectors (same thread,
   // same address, so it simply overwrites the first result).
   if (__builtin_expect(fix_mask != 0, 0)) {
 #pragma unroll
-    for (int u = 0; u < kVecs; ++u) {
-      if (!(fix_mask >> u & 1u)) continue;
-      // Opaque copies: keep the compiler from folding this pass into the first.
-      u32x4 x = kx[u];
-      uint32_t v = vi[u];
-      asm volatile("" : "+v"(x), "+v"(v));
-      const Where at = where(v);
-      double c[4], s[4];
-      pair_tables(p, pb, at.hrow16, at.wrow16, c, s);
+    for (int g = 0; g < kHeads; ++g) {
+      if (!(fix_mask >> g & 1u)) continue;
+      u32x4 x = kx[g];
+      asm volatile("" : "+v"(x));  // keeps this pass from being folded into the first
       FixDetect unused;
-      *reinterpret_cast<u32x4*>(kout + at.dst16) = rotate_vec<true>(x, c, s, unused);
+      *reinterpret_cast<u32x4*>(kout + dst_off + g * dst_head) = rotate_vec<true>(x, c, s, unused);
     }
   }
 }
 
-dim3 rows_grid(const RopeParams& p) {
-  const uint32_t per_block = kThreads * kVecs;
-  return dim3(((uint32_t)p.row_vecs + per_block - 1) / per_block, p.n_rows, 1);
+template <bool kAppend>
+hipError_t launch_rows(const RopeParams& p, hipStream_t s) {
+  const int lg = p.lg_cpr;
+  const uint32_t tpb = kThreads >> lg;
+  const dim3 grid((p.ft + tpb - 1) / tpb, p.n_rows, (p.n_heads + kHeads - 1) / kHeads);
+  if (lg == 4)
+    hipLaunchKernelGGL((rope_rows_kernel<kAppend, 4>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((rope_rows_kernel<kAppend, 3>), grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_rope3d(const RopeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(rope_rows_kernel<false>, rows_grid(p), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
-}
+hipError_t launch_rope3d(const RopeParams& p, hipStream_t s) { return launch_rows<false>(p, s); }
 
-hipError_t launch_kv_append(const RopeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(rope_rows_kernel<true>, rows_grid(p), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
-}
+hipError_t launch_kv_append(const RopeParams& p, hipStream_t s) { return launch_rows<true>(p, s); }
 
 }  // namespace wm

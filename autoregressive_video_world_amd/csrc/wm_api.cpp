@@ -148,6 +148,13 @@ struct wm_kvring {
   uint8_t* pool;
   std::vector<int64_t> n_committed, t0;
   std::vector<double> inv_t;
+  // t-band (cos, sin) rows by absolute t, direct-mapped: a frame's row is
+  // needed by every RoPE call of its denoise steps and by its append.
+  struct TRow {
+    int64_t t = INT64_MIN;
+    float2 cs[wm::kMaxTPairs];
+  };
+  mutable TRow t_cache[64];
 };
 
 namespace {
@@ -171,11 +178,16 @@ int64_t next_t(const wm_kvring* r, int b) { return r->t0[b] + r->n_committed[b];
 
 void t_row(const wm_kvring* r, int64_t t, float2* cs) {
   const int np = r->bands.dt / 2;
-  for (int j = 0; j < np; ++j) {
-    const double ang = (double)t * r->inv_t[j];
-    cs[j].x = (float)g_cos(ang);
-    cs[j].y = (float)g_sin(ang);
+  wm_kvring::TRow& c = r->t_cache[(uint64_t)t & 63];
+  if (c.t != t) {
+    for (int j = 0; j < np; ++j) {
+      const double ang = (double)t * r->inv_t[j];
+      c.cs[j].x = (float)g_cos(ang);
+      c.cs[j].y = (float)g_sin(ang);
+    }
+    c.t = t;
   }
+  memcpy(cs, c.cs, sizeof(float2) * np);
 }
 
 // Multiplier and shift for wm::FastDiv (d >= 1, dividends below 2^31):

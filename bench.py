@@ -188,27 +188,33 @@ def main():
 
     # ---- per-kernel timing with HIP events on the launch stream ------------
     # `reps` launches back to back between one pair of events: the mean
-    # duration of a launch in a busy stream (an event pair around a single
-    # short launch would add the idle stream's dispatch latency, several us).
-    def timed(fn, reps):
+    # duration of a launch in a busy stream.  Short launches (RoPE, append)
+    # are queued behind one attention launch, so that, as in a rollout, the
+    # host-side cost of each call (measured separately) overlaps GPU work
+    # instead of leaving the GPU idle between launches.
+    def timed(fn, reps, behind=None):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         fn()
         torch.cuda.synchronize()
+        if behind is not None:
+            behind()
         a.record(stream)
+        h0 = time.perf_counter()
         for _ in range(reps):
             fn()
+        host_us = (time.perf_counter() - h0) / reps * 1e6
         b.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+        return a.elapsed_time(b) / reps, host_us
 
     ring.rope3d(qs[0], C, y=q_rot)
     ring.rope3d(ks[0], C, y=k_rot)
-    attn_mean = timed(lambda: ring.chunk_attn(q_rot, k_rot, vs[0], C, out=outs[0], workspace=ws),
-                      args.kernel_reps)
-    rope_q_mean = timed(lambda: ring.rope3d(qs[0], C, y=q_rot), args.kernel_reps)
-    rope_k_mean = timed(lambda: ring.rope3d(ks[0], C, y=k_rot), args.kernel_reps)
-    app_mean = timed(lambda: ring.append_evict(ks[-1], vs[-1], C), args.kernel_reps)
+    attn = lambda: ring.chunk_attn(q_rot, k_rot, vs[0], C, out=outs[0], workspace=ws)
+    attn_mean, _ = timed(attn, args.kernel_reps)
+    rope_q_mean, rope_host_us = timed(lambda: ring.rope3d(qs[0], C, y=q_rot), args.kernel_reps, attn)
+    rope_k_mean, _ = timed(lambda: ring.rope3d(ks[0], C, y=k_rot), args.kernel_reps, attn)
+    app_mean, app_host_us = timed(lambda: ring.append_evict(ks[-1], vs[-1], C), args.kernel_reps, attn)
     torch.cuda.synchronize()
 
     attn_tflops = wl.attn_flops() / (attn_mean * 1e-3) / 1e12
@@ -246,10 +252,11 @@ def main():
                      "flops_per_launch": wl.attn_flops(), "split_workspace_bytes": ws_bytes},
         "append": {"bound": "hbm", "achieved": round(app_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": round(app_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": app_bytes,
-                   "launch_ms_mean": round(app_mean, 5)},
+                   "launch_ms_mean": round(app_mean, 5), "host_us_per_call": round(app_host_us, 1)},
         "rope": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
-                 "launch_ms_mean_q": round(rope_q_mean, 5), "launch_ms_mean_k": round(rope_k_mean, 5)},
+                 "launch_ms_mean_q": round(rope_q_mean, 5), "launch_ms_mean_k": round(rope_k_mean, 5),
+                 "host_us_per_call": round(rope_host_us, 1)},
         "cpu_baseline": None,
     }
     ring.close()
