@@ -3,8 +3,7 @@
 // Both kernels are HBM-bound streams over 16-byte vectors (8 bf16 = 4
 // rotation pairs of one (token, head) row).  Each thread owns the same
 // 16-byte slot of one token in kHeads heads and issues all of its loads
-// before any arithmetic, so a wave keeps 4 (rope) or 8 (append) 16-byte loads
-// in flight per lane.
+// before any arithmetic.
 //
 // Rotation, exactly: a bf16 value times an fp32 table entry is exact in fp64,
 // so y0 = x0*c - x1*s and y1 = x0*s + x1*c are each rounded once to fp64 (one
@@ -93,22 +92,30 @@ __device__ __forceinline__ u32x4 rotate_vec(u32x4 x, const double (&c)[4], const
 }
 
 // (cos, sin) of pair pr at the token (hpos, wpos): the t band from the row's
-// kernel-argument values, the h and w bands from the pool table.
+// kernel-argument values, the h and w bands from the pool table.  Both
+// entries are loaded unconditionally (t pairs read pool entry 0, h/w pairs
+// t entry 0) and blended as c = e_hw * keep + e_t with keep = 0, e_t = the t
+// value for t pairs (e_hw is finite and the t rows hold no -0, so this is
+// exactly the t value) and keep = 1, e_t = -0 for h/w pairs (exactly e_hw).
+// No branch, so no wait on the earlier loads sits between the lookups.
 __device__ __forceinline__ void pair_entry(const RopeParams& p, int row, int pr, uint32_t hpos,
                                            uint32_t wpos, double& c, double& s) {
-  if (pr < p.dt2) {
-    c = p.tcs[row][pr].x;
-    s = p.tcs[row][pr].y;
-  } else {
-    const uint32_t e = pr < p.dt2 + p.dh2
-                           ? hpos * p.dh2 + (pr - p.dt2)
-                           : p.w_base + wpos * p.dw2 + (pr - p.dt2 - p.dh2);
-    c = p.hw[e].x;
-    s = p.hw[e].y;
-  }
+  const bool in_t = pr < p.dt2;
+  const bool in_h = pr < p.dt2 + p.dh2;
+  const uint32_t e = in_t ? 0u
+                          : (in_h ? hpos * p.dh2 + (pr - p.dt2)
+                                  : p.w_base + wpos * p.dw2 + (pr - p.dt2 - p.dh2));
+  const float2 t = p.tcs[row][in_t ? pr : 0];
+  const double2 hw = p.hw[e];
+  const double keep = in_t ? 0.0 : 1.0;
+  c = __builtin_fma(hw.x, keep, in_t ? (double)t.x : -0.0);
+  s = __builtin_fma(hw.y, keep, in_t ? (double)t.y : -0.0);
 }
 
-// grid: x = ceil(ft / tokens per block), y = row of p.rows, z = ceil(n_heads / kHeads).
+// grid: x = ceil(ft / tokens per block), y = row of p.rows,
+//       z = head group (rope) or 2 * head group + part (append: part 0 rotates
+//       K, part 1 copies V; separate waves, so the V stream runs while K waves
+//       compute).
 // Thread = (token, 16-byte slot c8 of the head dim); it handles kHeads heads of
 // that token, so its four pairs' table entries and its token's position are
 // looked up once.  A wave covers 64 / (d/8) consecutive tokens: each head's
@@ -122,48 +129,58 @@ __global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p)
   const uint32_t c8 = threadIdx.x & (kCpr - 1);
   const uint32_t tok = blockIdx.x * kTpb + (threadIdx.x >> kLgCpr);
   if (tok >= (uint32_t)p.ft) return;
-  const int h0 = blockIdx.z * kHeads;
+  const int hgroup = kAppend ? (int)(blockIdx.z >> 1) : (int)blockIdx.z;
+  const bool v_part = kAppend && (blockIdx.z & 1);
+  const int h0 = hgroup * kHeads;
   const int nh = min(kHeads, p.n_heads - h0);
   const int rb = p.rows[row].b;
   const int rj = p.rows[row].j;
   const uint32_t head_bytes = (uint32_t)kCpr * 16u;
 
-  // Loads first (heads past the last are clamped; their stores are skipped).
   // A frame of the chunk holds below 2^28 elements: 32-bit byte offsets.
+  // Heads past the last are clamped on load; their stores are skipped.
   const int64_t row_base = (int64_t)rb * p.x_b_stride + (int64_t)rj * p.ft * p.n_heads * (kCpr * 8);
   const uint32_t src_off = ((tok * (uint32_t)p.n_heads + h0) * kCpr + c8) * 16u;
-  const char* xs = reinterpret_cast<const char*>(p.x + row_base) + src_off;
-  const char* vs = reinterpret_cast<const char*>(p.vsrc + row_base) + src_off;
-  u32x4 kx[kHeads], vx[kHeads];
-#pragma unroll
-  for (int g = 0; g < kHeads; ++g) {
-    const uint32_t off = (uint32_t)(g < nh ? g : nh - 1) * head_bytes;
-    kx[g] = *reinterpret_cast<const u32x4*>(xs + off);
-    if constexpr (kAppend) vx[g] = *reinterpret_cast<const u32x4*>(vs + off);
+
+  // Destinations: the chunk layout (rope) or the slot's [head][token][d] block.
+  char* out;
+  uint32_t dst_off, dst_head;
+  if constexpr (kAppend) {
+    const int64_t slot_base =
+        ((int64_t)rb * p.ring_slots + p.rows[row].slot) * p.n_heads * p.ft * (kCpr * 8);
+    out = reinterpret_cast<char*>((v_part ? p.vdst : p.y) + slot_base);
+    dst_head = (uint32_t)p.ft * head_bytes;
+    dst_off = (uint32_t)h0 * dst_head + (tok * kCpr + c8) * 16u;
+  } else {
+    out = reinterpret_cast<char*>(p.y + row_base);
+    dst_head = head_bytes;
+    dst_off = src_off;
   }
 
+  if (v_part) {  // V: a plain copy into the slot
+    const char* vs = reinterpret_cast<const char*>(p.vsrc + row_base) + src_off;
+    u32x4 vx[kHeads];
+#pragma unroll
+    for (int g = 0; g < kHeads; ++g)
+      vx[g] = *reinterpret_cast<const u32x4*>(vs + (uint32_t)(g < nh ? g : nh - 1) * head_bytes);
+#pragma unroll
+    for (int g = 0; g < kHeads; ++g)
+      if (g < nh) *reinterpret_cast<u32x4*>(out + dst_off + g * dst_head) = vx[g];
+    return;
+  }
+
+  // Table entries first (L2 hits), then the K loads (HBM).
   const uint32_t hpos = fast_div(tok, p.div_fw);
   const uint32_t wpos = tok - hpos * p.fw;
   double c[4], s[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) pair_entry(p, row, (int)c8 * 4 + k, hpos, wpos, c[k], s[k]);
 
-  // Destinations: the chunk layout (rope) or the slot's [head][token][d] block.
-  char* kout;
-  char* vout = nullptr;
-  uint32_t dst_off, dst_head;
-  if constexpr (kAppend) {
-    const int64_t slot_base =
-        ((int64_t)rb * p.ring_slots + p.rows[row].slot) * p.n_heads * p.ft * (kCpr * 8);
-    kout = reinterpret_cast<char*>(p.y + slot_base);
-    vout = reinterpret_cast<char*>(p.vdst + slot_base);
-    dst_head = (uint32_t)p.ft * head_bytes;
-    dst_off = (uint32_t)h0 * dst_head + (tok * kCpr + c8) * 16u;
-  } else {
-    kout = reinterpret_cast<char*>(p.y + row_base);
-    dst_head = head_bytes;
-    dst_off = src_off;
-  }
+  const char* xs = reinterpret_cast<const char*>(p.x + row_base) + src_off;
+  u32x4 kx[kHeads];
+#pragma unroll
+  for (int g = 0; g < kHeads; ++g)
+    kx[g] = *reinterpret_cast<const u32x4*>(xs + (uint32_t)(g < nh ? g : nh - 1) * head_bytes);
 
   uint32_t fix_mask = 0;
 #pragma unroll
@@ -172,8 +189,7 @@ __global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p)
     const u32x4 o = rotate_vec<false>(kx[g], c, s, det);
     if (g >= nh) continue;
     fix_mask |= (uint32_t)det.needed() << g;
-    *reinterpret_cast<u32x4*>(kout + dst_off + g * dst_head) = o;
-    if constexpr (kAppend) *reinterpret_cast<u32x4*>(vout + dst_off + g * dst_head) = vx[g];
+    *reinterpret_cast<u32x4*>(out + dst_off + g * dst_head) = o;
   }
 
   // Rare second pass: exact recomputation of flagged vectors (same thread,
@@ -185,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p)
       u32x4 x = kx[g];
       asm volatile("" : "+v"(x));  // keeps this pass from being folded into the first
       FixDetect unused;
-      *reinterpret_cast<u32x4*>(kout + dst_off + g * dst_head) = rotate_vec<true>(x, c, s, unused);
+      *reinterpret_cast<u32x4*>(out + dst_off + g * dst_head) = rotate_vec<true>(x, c, s, unused);
     }
   }
 }
@@ -194,7 +210,8 @@ template <bool kAppend>
 hipError_t launch_rows(const RopeParams& p, hipStream_t s) {
   const int lg = p.lg_cpr;
   const uint32_t tpb = kThreads >> lg;
-  const dim3 grid((p.ft + tpb - 1) / tpb, p.n_rows, (p.n_heads + kHeads - 1) / kHeads);
+  const dim3 grid((p.ft + tpb - 1) / tpb, p.n_rows,
+                  (kAppend ? 2 : 1) * ((p.n_heads + kHeads - 1) / kHeads));
   if (lg == 4)
     hipLaunchKernelGGL((rope_rows_kernel<kAppend, 4>), grid, dim3(kThreads), 0, s, p);
   else
