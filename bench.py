@@ -48,11 +48,11 @@ def parse():
 
 
 def kernel_source_digest():
-    """sha256 over the attention kernel source, the internal header and the build flags."""
+    """sha256 over the kernel sources, the internal header and the build flags."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "autoregressive_video_world_amd", "csrc")
-    for rel in ("kernels/chunk_attn.hip", "wm_internal.hpp"):
+    for rel in ("kernels/chunk_attn.hip", "kernels/rope_append.hip", "wm_internal.hpp"):
         with open(os.path.join(csrc, rel), "rb") as f:
             h.update(f.read())
     with open(os.path.join(ROOT, "autoregressive_video_world_amd", "_build.py"), "rb") as f:
@@ -60,11 +60,11 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def profiled_traffic(workload_name):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary, or None.
+def profiled_traffic(workload_name, key="traffic_bytes_per_launch"):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
 
-    The summary records the source digest of the kernel it measured; a kernel
-    changed since then gets None (stale counters are not reported)."""
+    The summary records the source digest of the kernels it measured; kernels
+    changed since then get None (stale counters are not reported)."""
     path = os.path.join(ROOT, "profiles", "chunk_attn_%s_hbm_traffic.md" % workload_name)
     if not os.path.exists(path):
         return None
@@ -77,7 +77,7 @@ def profiled_traffic(workload_name):
     if fields.get("source_sha256") != kernel_source_digest():
         return None
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        return int(fields[key])
     except (KeyError, ValueError):
         return None
 
@@ -252,6 +252,7 @@ def main():
                      "flops_per_launch": wl.attn_flops(), "split_workspace_bytes": ws_bytes},
         "append": {"bound": "hbm", "achieved": round(app_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": round(app_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": app_bytes,
+                   "traffic": profiled_traffic(wl.name, "append_traffic_bytes_per_launch"),
                    "launch_ms_mean": round(app_mean, 5), "host_us_per_call": round(app_host_us, 1)},
         "rope": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
