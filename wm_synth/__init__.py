@@ -127,15 +127,24 @@ class Source:
         h = self.wl.n_q_heads if kind == "q" else self.wl.n_kv_heads
         return (self.wl.ft, h, self.wl.head_dim)
 
+    @staticmethod
+    def pool_index(b, n, s):
+        """Pool entry of (rollout b, frame n, denoise step s) in the long workload."""
+        return (7919 * b + 31 * n + s) % POOL_ENTRIES
+
+    def pool_entry(self, e, kind):
+        """uint16 (Ft, H, d) pool entry e of the long workload (cached)."""
+        key = (e, kind)
+        if key not in self._pool:
+            scale = self.q_scale if kind == "q" else 1.0
+            self._pool[key] = _draw([self.wl.cfg, 0, e, 0, KINDS[kind]], self.shape(kind), scale)
+        return self._pool[key]
+
     def frame(self, b, n, s, kind):
         """uint16 (Ft, H, d) draw for rollout b, frame n, denoise step s (-1 = prefill)."""
-        scale = self.q_scale if kind == "q" else 1.0
         if self.wl.cfg == 5:
-            e = (7919 * b + 31 * n + s) % POOL_ENTRIES
-            key = (e, kind)
-            if key not in self._pool:
-                self._pool[key] = _draw([self.wl.cfg, 0, e, 0, KINDS[kind]], self.shape(kind), scale)
-            return self._pool[key]
+            return self.pool_entry(self.pool_index(b, n, s), kind)
+        scale = self.q_scale if kind == "q" else 1.0
         return _draw([self.wl.cfg, b, n, s + 1, KINDS[kind]], self.shape(kind), scale)
 
     def chunk(self, b, n0, n_frames, s, kind):
