@@ -57,19 +57,24 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kKT = 64;                // keys per tile
 constexpr int kXcds = 8;               // MI355X: 8 accelerator complex dies
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 constexpr int kColPitch = kKT * 16 + 64;  // bytes per 16-byte column of a tile
 
-template <int HD>
+// NQB = 32-query blocks per wave task: 2 -> 4 waves per workgroup, one per
+// SIMD, 64 queries per wave (launched); 1 -> 8 waves, two per SIMD, 32
+// queries each (kept compilable; slower, since each K/V fragment read from
+// LDS then feeds half as many MFMAs).  A workgroup covers 256 queries of one
+// kv head either way.
+template <int HD, int NQB>
 struct Cfg {
+  static constexpr int WAVES = 8 / NQB;
+  static constexpr int THREADS = WAVES * 64;
   static constexpr int NDC = HD / 16;             // 16-wide d chunks (QK^T contraction)
   static constexpr int NDB = HD / 32;             // 32-row d blocks (PV output)
   static constexpr int NCOL = HD / 8;             // 16-byte columns per key row
-  static constexpr int COLS_PER_WAVE = NCOL / kWaves;
+  static constexpr int COLS_PER_WAVE = NCOL / WAVES;
   static constexpr int TILE_BYTES = NCOL * kColPitch;
   static constexpr int LDS_BYTES = 6 * TILE_BYTES;  // K x3, V x3
 };
@@ -127,9 +132,9 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int HD, bool kSmallFt>
-__global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParams p) {
-  using C = Cfg<HD>;
+template <int HD, int NQB>
+__global__ __launch_bounds__(512 / NQB, 1) void chunk_attn_kernel(const AttnParams p) {
+  using C = Cfg<HD, NQB>;
   // Six distinct LDS objects (not one array): the compiler can then prove that
   // a read of one buffer never aliases a DMA still writing another, and does
   // not stall the read on vmcnt(0).
@@ -168,18 +173,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   const int t_begin = split * tps;
   const int n_local = min(ntiles, t_begin + tps) - t_begin;
 
-  const int task = wgi * kWaves + wave;
+  const int task = wgi * C::WAVES + wave;
   const bool has_task = task < p.group * p.nqb;
   const int qblk = has_task ? task / p.group : 0;
   const int h = g * p.group + (has_task ? task % p.group : 0);
-  const int q0 = qblk * 64;
+  const int q0 = qblk * 32 * NQB;
 
   // A key-range split past the end of a short rollout's keys (ragged batch):
   // record an empty partial (sum 0) and leave; the whole workgroup agrees.
   if (n_local <= 0) {
     if (has_task && lane < 32) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < NQB; ++qb) {
         const int q = q0 + qb * 32 + lane;
         if (q < p.nq) {
           const int64_t row = (((int64_t)split * p.nb + bi) * p.nq + q) * p.hq + h;
@@ -192,9 +197,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   }
 
   // ---- Q^T operands: lane (l32, hi) holds query q0+qb*32+l32, d = dc*16+hi*8.. --
-  bf16x8 qreg[2][C::NDC];
+  bf16x8 qreg[NQB][C::NDC];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     const int q = min(q0 + qb * 32 + l32, p.nq - 1);
     const uint16_t* src = p.q + (((int64_t)b * p.nq + q) * p.hq + h) * HD + hi * 8;
 #pragma unroll
@@ -237,15 +242,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   };
 
   // ---- running state ------------------------------------------------------
-  f32x16 oacc[C::NDB][2];
+  f32x16 oacc[C::NDB][NQB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[db][qb][i] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY};  // running max (scaled, log2 domain)
-  float l_run[2] = {0.f, 0.f};              // running sum over this lane's keys
+  float m_run[NQB], l_run[NQB];  // running max (scaled, log2 domain), sum over this lane's keys
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
   const float sl2 = p.scale_log2e;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -260,23 +269,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
 
   // S^T of a 32-key sub-tile (keys kb*32.. of the tile) for both query blocks:
   // each K fragment read from LDS feeds two MFMAs.
-  auto qk = [&](const lds_u8* tile, int kb, f32x16 (&S)[2]) __attribute__((always_inline)) {
+  auto qk = [&](const lds_u8* tile, int kb, f32x16 (&S)[NQB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int dc = 0; dc < C::NDC; ++dc) {
       const bf16x8 kf = *(const lds_bf16x8*)(tile + k_off + 2 * dc * kColPitch + kb * 512);
-      if (dc == 0) {
-        S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[0][0], (f32x16){}, 0, 0, 0);
-        S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[1][0], (f32x16){}, 0, 0, 0);
-      } else {
-        S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[0][dc], S[0], 0, 0, 0);
-        S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[1][dc], S[1], 0, 0, 0);
-      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+        S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[qb][dc], dc == 0 ? (f32x16){} : S[qb], 0, 0, 0);
     }
   };
   // O^T += V^T P^T over a 32-key sub-tile, both query blocks; each V^T fragment
   // (two transposed reads) feeds two MFMAs.  MFMA half h covers keys kb*32+16h..:
   // lane half hi takes keys +4*hi+{0..3} and +8+4*hi+{0..3}.
-  auto pv = [&](const lds_u8* tile, int kb, const bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
+  auto pv = [&](const lds_u8* tile, int kb, const bf16x8 (&P)[NQB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
@@ -285,15 +290,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
         const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * 16));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, (s16x8){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
-        oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[0][half], oacc[db][0], 0, 0, 0);
-        oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[1][half], oacc[db][1], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[qb][half], oacc[db][qb], 0, 0, 0);
       }
     }
   };
   // P^T fragments of a sub-tile: exp2(s*scale*log2e - m) in bf16, and row sums.
-  auto softmax = [&](const f32x16 (&S)[2], bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
+  auto softmax = [&](const f32x16 (&S)[NQB], bf16x8 (&P)[NQB][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       const float mneg = -m_run[qb];
       uint32_t pk[8];
 #pragma unroll
@@ -320,13 +326,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
     return xhalf_max(fmaxf(m0, m1));
   };
   // Mask keys >= nvalid of a sub-tile (only in the last tile of the key range).
-  auto mask_sub = [&](f32x16 (&S)[2], int nvalid) __attribute__((always_inline)) {
+  auto mask_sub = [&](f32x16 (&S)[NQB], int nvalid) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = (i >> 2) * 8 + hi * 4 + (i & 3);
       if (key >= nvalid) {
-        S[0][i] = -INFINITY;
-        S[1][i] = -INFINITY;
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) S[qb][i] = -INFINITY;
       }
     }
   };
@@ -334,11 +340,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   // taken before its exponentials: the running max and sum move at once, but
   // O is rescaled only after the still-pending P(j-1)*V -- formed against the
   // old max -- has been accumulated (rescale_o at the end of the sub-step).
-  auto rescale_decide = [&](const float (&mx)[2], float (&alpha)[2]) __attribute__((always_inline)) {
-    const bool need = (mx[0] * sl2 > m_run[0] + kRescaleSlack) | (mx[1] * sl2 > m_run[1] + kRescaleSlack);
+  auto rescale_decide = [&](const float (&mx)[NQB], float (&alpha)[NQB]) __attribute__((always_inline)) {
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) need |= mx[qb] * sl2 > m_run[qb] + kRescaleSlack;
     if (!__builtin_amdgcn_ballot_w64(need)) return false;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       const float m_new = fmaxf(m_run[qb], mx[qb] * sl2);
       alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
       m_run[qb] = m_new;
@@ -346,12 +354,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
     }
     return true;
   };
-  auto rescale_o = [&](const float (&alpha)[2]) __attribute__((always_inline)) {
+  auto rescale_o = [&](const float (&alpha)[NQB]) __attribute__((always_inline)) {
     // A side-effecting marker keeps this block a real (rarely taken) branch:
     // if-converted, it would cost 3 x 128 VALU operations on every sub-step.
     asm volatile("; rescale O" ::: "memory");
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
@@ -362,30 +370,30 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   // Sub-tile j of the local key range: mask what lies past the end, then the
   // rescale decision on its row max.
   const int nk_local = nk - t_begin * kKT;  // keys of this split's range (last tile may be partial)
-  auto prepare = [&](int j, f32x16 (&S)[2], float (&mx)[2], float (&alpha)[2]) __attribute__((always_inline)) {
+  auto prepare = [&](int j, f32x16 (&S)[NQB], float (&mx)[NQB], float (&alpha)[NQB]) __attribute__((always_inline)) {
     const int nvalid = nk_local - j * 32;
     if (nvalid < 32) {
       mask_sub(S, nvalid);
-      mx[0] = sub_rowmax(S[0]);
-      mx[1] = sub_rowmax(S[1]);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) mx[qb] = sub_rowmax(S[qb]);
     }
     return rescale_decide(mx, alpha);
   };
-  f32x16 SA[2], SB[2];
-  bf16x8 PA[2][2], PB[2][2];
-  float mx[2];
+  f32x16 SA[NQB], SB[NQB];
+  bf16x8 PA[NQB][2], PB[NQB][2];
+  float mx[NQB];
   const uint16_t *kp, *vp;
   // S of the sub-tile whose softmax is next, copied once out of the MFMA
   // accumulators into VGPRs (the row max and the exponentials then read the
   // copy: one AGPR read per value instead of two).
-  f32x16 Sv[2];
-  auto take_s = [&](const f32x16 (&S)[2]) __attribute__((always_inline)) {
-    Sv[0] = S[0];
-    Sv[1] = S[1];
-    pin_vgpr(Sv[0]);
-    pin_vgpr(Sv[1]);
-    mx[0] = sub_rowmax(Sv[0]);
-    mx[1] = sub_rowmax(Sv[1]);
+  f32x16 Sv[NQB];
+  auto take_s = [&](const f32x16 (&S)[NQB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      Sv[qb] = S[qb];
+      pin_vgpr(Sv[qb]);
+      mx[qb] = sub_rowmax(Sv[qb]);
+    }
   };
 
   // Prologue: tiles 0 and 1 into LDS; S and row max of sub-tile 0.
@@ -415,23 +423,24 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
   auto tile_steps = [&](int u, bool first, lds_u8* ku, lds_u8* kn, lds_u8* kf, lds_u8* vu,
                         lds_u8* vp_) __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      pin_agpr(oacc[db][0]);
-      pin_agpr(oacc[db][1]);
-    }
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) pin_agpr(oacc[db][qb]);
     row_ptrs(u + 2, kp, vp);
     dma_cols(kp, kf);
-    float alpha[2];
+    float alpha[NQB];
     // sub-step 2u: S(2u) in SA, P(2u-1) in PB
     bool resc = prepare(2 * u, Sv, mx, alpha);
     qk(ku, 1, SB);
     softmax(Sv, PA);
     if (!first) pv(vp_, 1, PB);
-    anchor(PA[0][0]);
-    anchor(PA[0][1]);
-    anchor(PA[1][0]);
-    anchor(PA[1][1]);
     take_s(SB);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      anchor(PA[qb][0]);
+      anchor(PA[qb][1]);
+      anchor(mx[qb]);
+    }
     if (resc) rescale_o(alpha);
     tile_barrier<2 * C::COLS_PER_WAVE>();
     // sub-step 2u+1: S(2u+1) in SB, P(2u) in PA
@@ -440,11 +449,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
     qk(kn, 0, SA);
     softmax(Sv, PB);
     pv(vu, 0, PA);
-    anchor(PB[0][0]);
-    anchor(PB[0][1]);
-    anchor(PB[1][0]);
-    anchor(PB[1][1]);
     take_s(SA);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      anchor(PB[qb][0]);
+      anchor(PB[qb][1]);
+      anchor(mx[qb]);
+    }
     if (resc) rescale_o(alpha);
   };
   tile_steps(0, true, K0, K1, K2, V0, V2);
@@ -469,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_attn_kernel(const AttnParam
 
   // ---- epilogue -------------------------------------------------------------
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     const int q = q0 + qb * 32 + l32;
     const float l_tot = xhalf_sum(l_run[qb]);
     if (q >= p.nq) continue;
@@ -558,18 +569,11 @@ hipError_t launch_chunk_attn(const AttnParams& p_in, int head_dim, hipStream_t s
   p.n_wg = p.nb * p.hkv * p.wg_per_bg * p.nsplit;
   p.per_xcd = (p.n_wg + kXcds - 1) / kXcds;
   const dim3 grid(p.per_xcd * kXcds);
-  const bool small = p.ft < 4;
-  if (head_dim == 128) {
-    if (small)
-      hipLaunchKernelGGL((chunk_attn_kernel<128, true>), grid, dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL((chunk_attn_kernel<128, false>), grid, dim3(kThreads), 0, s, p);
-  } else {
-    if (small)
-      hipLaunchKernelGGL((chunk_attn_kernel<64, true>), grid, dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL((chunk_attn_kernel<64, false>), grid, dim3(kThreads), 0, s, p);
-  }
+  if (p.wave_qblocks != 2) return hipErrorInvalidValue;
+  if (head_dim == 128)
+    hipLaunchKernelGGL((chunk_attn_kernel<128, 2>), grid, dim3(Cfg<128, 2>::THREADS), 0, s, p);
+  else
+    hipLaunchKernelGGL((chunk_attn_kernel<64, 2>), grid, dim3(Cfg<64, 2>::THREADS), 0, s, p);
   if (p.nsplit > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -74,7 +74,8 @@ struct AttnParams {
   int32_t ft;             // tokens per frame
   int32_t nq;             // queries per rollout = n_frames * Ft
   int32_t ring_slots;     // R = S + W
-  int32_t nqb;            // 64-query blocks per rollout
+  int32_t wave_qblocks;   // 32-query blocks per wave task (1 or 2)
+  int32_t nqb;            // wave-task query blocks (32 * wave_qblocks queries) per rollout
   int32_t wg_per_bg;      // workgroups per (rollout, kv head) per split
   int32_t nsplit;         // key-range splits (1 = none)
   int32_t n_wg;           // logical workgroups (set by the launcher)
