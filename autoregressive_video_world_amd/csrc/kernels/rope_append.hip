@@ -3,7 +3,8 @@
 // Both kernels are HBM-bound streams over 16-byte vectors (8 bf16 = 4
 // rotation pairs of one (token, head) row).  Each thread owns the same
 // 16-byte slot of one token in kHeads heads and issues all of its loads
-// before any arithmetic.
+// before any arithmetic.  Results are written with the non-temporal hint
+// (streamed out instead of being kept in the caches: measurably faster).
 //
 // Rotation, exactly: a bf16 value times an fp32 table entry is exact in fp64,
 // so y0 = x0*c - x1*s and y1 = x0*s + x1*c are each rounded once to fp64 (one
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p)
       vx[g] = *reinterpret_cast<const u32x4*>(vs + (uint32_t)(g < nh ? g : nh - 1) * head_bytes);
 #pragma unroll
     for (int g = 0; g < kHeads; ++g)
-      if (g < nh) *reinterpret_cast<u32x4*>(out + dst_off + g * dst_head) = vx[g];
+      if (g < nh) __builtin_nontemporal_store(vx[g], reinterpret_cast<u32x4*>(out + dst_off + g * dst_head));
     return;
   }
 
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p)
     const u32x4 o = rotate_vec<false>(kx[g], c, s, det);
     if (g >= nh) continue;
     fix_mask |= (uint32_t)det.needed() << g;
-    *reinterpret_cast<u32x4*>(out + dst_off + g * dst_head) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + dst_off + g * dst_head));
   }
 
   // Rare second pass: exact recomputation of flagged vectors (same thread,
