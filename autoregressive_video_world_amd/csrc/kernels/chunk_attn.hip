@@ -25,7 +25,9 @@
 //    each lane owns one query column and 16 keys, so the row max and row sum
 //    need one cross-half exchange (v_permlane32_swap), no tree;
 //  * O^T += V^T * P^T on the same MFMA: P^T comes straight from the S^T
-//    accumulator (exp2, cvt_pk_bf16).  V^T operands are read with
+//    accumulator (exp2, cvt_pk_bf16); the row sum l adds the fp32
+//    exponentials (plain adds: on this chip a v_dot2 does not issue beside a
+//    running MFMA, fp32 adds do).  V^T operands are read with
 //    ds_read_b64_tr_b16: in each 16-lane group, lane j receives element j%4
 //    of the 8-byte chunks read by lanes j/4, j/4+4, j/4+8, j/4+12, so when
 //    lane L reads key row kbase + L/4 at dims dbase + 4*(L%4), lane j gets
@@ -33,7 +35,8 @@
 //    exactly the keys the S^T accumulator layout gives that lane's P;
 //  * 32-key sub-tile pipeline: in sub-step j the matrix cores compute S of
 //    sub-tile j+1 and O += V P of sub-tile j-1 while the vector ALUs form P of
-//    sub-tile j.  Each K and V fragment read from LDS feeds both query
+//    sub-tile j, interleaved by hand (one MFMA per slot with a slice of the
+//    vector work).  Each K and V fragment read from LDS feeds both query
 //    blocks (LDS instruction count per tile halves compared with handling the
 //    blocks apart -- LDS issue, not bandwidth, is the scarce resource);
 //  * online softmax in the log2 domain with a lazy rescale: the running max
@@ -212,13 +215,16 @@ __global__ __launch_bounds__(512 / NQB, 1) void chunk_attn_kernel(const AttnPara
   // ---- tile loads: lane = key row, wave w fills columns w*CPW .. ------------
   const int ft = p.ft;
   const float inv_ft = 1.0f / (float)ft;
-  const uint16_t* const ring_k = p.pk + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD;
-  const uint16_t* const ring_v = p.pv + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD;
+  // This wave's first column, as a wave-uniform value (readfirstlane): the
+  // column offsets then fold into the base pointers and the LDS addresses
+  // (M0) are formed with scalar instructions.
+  const int col0 = __builtin_amdgcn_readfirstlane(wave) * C::COLS_PER_WAVE;
+  const uint16_t* const ring_k = p.pk + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD + col0 * 8;
+  const uint16_t* const ring_v = p.pv + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD + col0 * 8;
   const uint32_t slot_stride = (uint32_t)p.hkv * ft * HD;  // elements; < 2^31 per rollout
-  const uint16_t* const chunk_k = p.kc + ((int64_t)b * p.nq * p.hkv + g) * HD;
-  const uint16_t* const chunk_v = p.vc + ((int64_t)b * p.nq * p.hkv + g) * HD;
+  const uint16_t* const chunk_k = p.kc + ((int64_t)b * p.nq * p.hkv + g) * HD + col0 * 8;
+  const uint16_t* const chunk_v = p.vc + ((int64_t)b * p.nq * p.hkv + g) * HD + col0 * 8;
   const uint32_t chunk_stride = (uint32_t)p.hkv * HD;
-  const int col0 = wave * C::COLS_PER_WAVE;
 
   // Row pointers (K and V) of this lane's key row in local tile u.
   auto row_ptrs = [&](int u, const uint16_t*& kp, const uint16_t*& vp) __attribute__((always_inline)) {
@@ -233,11 +239,12 @@ __global__ __launch_bounds__(512 / NQB, 1) void chunk_attn_kernel(const AttnPara
     kp = in_ring ? ring_k + ro : chunk_k + co;
     vp = in_ring ? ring_v + ro : chunk_v + co;
   };
+  // rp: this lane's key row, already offset to column col0.
   auto dma_cols = [&](const uint16_t* rp, lds_u8* tile) __attribute__((always_inline)) {
+    lds_u8* const t0 = tile + col0 * kColPitch;
 #pragma unroll
     for (int i = 0; i < C::COLS_PER_WAVE; ++i) {
-      const int c = col0 + i;
-      __builtin_amdgcn_global_load_lds(rp + c * 8, tile + c * kColPitch, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(rp + i * 8, t0 + i * kColPitch, 16, 0, 0);
     }
   };
 
@@ -256,7 +263,6 @@ __global__ __launch_bounds__(512 / NQB, 1) void chunk_attn_kernel(const AttnPara
     l_run[qb] = 0.f;
   }
   const float sl2 = p.scale_log2e;
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // LDS byte offsets of this lane's reads inside a tile.
   //  K operand (A of S^T): key row kb*32 + l32, column 2*dc + hi.
@@ -296,26 +302,8 @@ __global__ __launch_bounds__(512 / NQB, 1) void chunk_attn_kernel(const AttnPara
       }
     }
   };
-  // P^T fragments of a sub-tile: exp2(s*scale*log2e - m) in bf16, and row sums.
-  auto softmax = [&](const f32x16 (&S)[NQB], bf16x8 (&P)[NQB][2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const float mneg = -m_run[qb];
-      uint32_t pk[8];
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][i], sl2, mneg));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][i + 1], sl2, mneg));
-        const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
-        l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[qb], false);
-        pk[i >> 1] = __builtin_bit_cast(uint32_t, pr);
-      }
-      P[qb][0] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-      P[qb][1] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
-    }
-  };
   // Row max over a 32-key sub-tile (lane pair holds the 32 keys of a query).
-  auto sub_rowmax = [&](const f32x16& S) __attribute__((always_inline)) {
+  auto sub_rowmax = [&](const auto& S) __attribute__((always_inline)) {
     float m0 = fmaxf(S[0], fmaxf(S[1], S[2]));
     float m1 = fmaxf(S[3], fmaxf(S[4], S[5]));
 #pragma unroll
@@ -326,7 +314,7 @@ __global__ __launch_bounds__(512 / NQB, 1) void chunk_attn_kernel(const AttnPara
     return xhalf_max(fmaxf(m0, m1));
   };
   // Mask keys >= nvalid of a sub-tile (only in the last tile of the key range).
-  auto mask_sub = [&](f32x16 (&S)[NQB], int nvalid) __attribute__((always_inline)) {
+  auto mask_sub = [&](auto& S, int nvalid) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = (i >> 2) * 8 + hi * 4 + (i & 3);
@@ -370,7 +358,7 @@ __global__ __launch_bounds__(512 / NQB, 1) void chunk_attn_kernel(const AttnPara
   // Sub-tile j of the local key range: mask what lies past the end, then the
   // rescale decision on its row max.
   const int nk_local = nk - t_begin * kKT;  // keys of this split's range (last tile may be partial)
-  auto prepare = [&](int j, f32x16 (&S)[NQB], float (&mx)[NQB], float (&alpha)[NQB]) __attribute__((always_inline)) {
+  auto prepare = [&](int j, auto& S, float (&mx)[NQB], float (&alpha)[NQB]) __attribute__((always_inline)) {
     const int nvalid = nk_local - j * 32;
     if (nvalid < 32) {
       mask_sub(S, nvalid);
@@ -385,14 +373,137 @@ __global__ __launch_bounds__(512 / NQB, 1) void chunk_attn_kernel(const AttnPara
   const uint16_t *kp, *vp;
   // S of the sub-tile whose softmax is next, copied once out of the MFMA
   // accumulators into VGPRs (the row max and the exponentials then read the
-  // copy: one AGPR read per value instead of two).
-  f32x16 Sv[NQB];
+  // copy: one AGPR read per value instead of two).  Separate scalars, not a
+  // vector: each value is then its own register, consumed independently.
+  float Sv[NQB][16];
   auto take_s = [&](const f32x16 (&S)[NQB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      Sv[qb] = S[qb];
-      pin_vgpr(Sv[qb]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        Sv[qb][i] = S[qb][i];
+        pin_vgpr(Sv[qb][i]);
+      }
       mx[qb] = sub_rowmax(Sv[qb]);
+    }
+  };
+
+  // One 32-key sub-step j, scheduled by hand.  Matrix op i is issued in slot i
+  // together with a slice of the vector work, and sched_barrier(0) keeps every
+  // slice in its slot (left alone, the scheduler clusters the matrix ops and
+  // the vector work then runs beside only a few of them):
+  //   slots [0, NQK):        S(j+1) = K Q^T, 2 MFMAs per K fragment
+  //                          || P(j) = exp2(S(j) * scale - m): 8 key pairs per query block
+  //   slots [NQK, NQK+NPV):  O += V^T P(j-1)^T, 2 MFMAs per V fragment
+  //                          || S(j+1) copied out of the accumulators, its row max;
+  //                             the DMA issue of this sub-step
+  // K fragments are read KAHEAD slots ahead of their MFMAs, V fragments
+  // during the last QK slots.
+  constexpr int NQK = C::NDC * NQB;
+  constexpr int NPV = C::NDB * 2 * NQB;
+  constexpr int NE = 8 * NQB;                 // exponential units (2 keys of one query block)
+  constexpr int E_PER = (NE + NQK - 1) / NQK;  // per QK slot
+  constexpr int KAHEAD = 4;
+  constexpr int NVF = C::NDB * 2;             // V fragments per sub-step
+  constexpr int VSLOT0 = NQK - NVF / 2 > 0 ? NQK - NVF / 2 : 0;  // first slot with V reads (2 per slot)
+  auto substep = [&](const lds_u8* kt, int kb, f32x16 (&Sn)[NQB], bf16x8 (&Po)[NQB][2],
+                     const lds_u8* vt, int vkb, const bf16x8 (&Pi)[NQB][2], bool do_pv,
+                     auto&& dma) __attribute__((always_inline)) {
+    bf16x8 kfr[C::NDC];
+    bf16x8 vfr[NVF];
+    uint32_t pk[NQB][8];
+    float mq[NQB][4];
+    float mneg[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) mneg[qb] = -m_run[qb];
+    auto read_k = [&](int dc) __attribute__((always_inline)) {
+      kfr[dc] = *(const lds_bf16x8*)(kt + k_off + 2 * dc * kColPitch + kb * 512);
+    };
+    auto read_v = [&](int f) __attribute__((always_inline)) {  // f = half * NDB + db
+      const int half = f / C::NDB, db = f % C::NDB;
+      const lds_u8* a = vt + v_off + db * 4 * kColPitch + (vkb * 32 + half * 16) * 16;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
+      const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * 16));
+      vfr[f] = __builtin_bit_cast(bf16x8, (s16x8){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+    };
+    // The slot's inputs pass through a volatile empty asm and its results into
+    // one: volatile asm keeps its order relative to sched_barrier, so neither
+    // the IR optimizers nor the scheduler can move the work out of its slot.
+    auto exp_unit = [&](int e) __attribute__((always_inline)) {
+      const int qb = e / 8, pr = e % 8;
+      float s0 = Sv[qb][2 * pr], s1 = Sv[qb][2 * pr + 1];
+      asm volatile("" : "+v"(s0), "+v"(s1));
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, sl2, mneg[qb]));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, sl2, mneg[qb]));
+      const bf16x2 two = {(__bf16)e0, (__bf16)e1};
+      l_run[qb] = (l_run[qb] + e0) + e1;  // fp32 adds: a dot instruction would not overlap the MFMAs
+      pk[qb][pr] = __builtin_bit_cast(uint32_t, two);
+      asm volatile("" ::"v"(pk[qb][pr]), "v"(l_run[qb]));
+    };
+    // copy 4 values of S(j+1) out of the accumulators, and their max
+    auto copy_unit = [&](int t) __attribute__((always_inline)) {
+      const int qb = t / 4, r = t % 4;
+      float x[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[k] = Sn[qb][4 * r + k];
+        asm volatile("" : "+v"(x[k]));
+        Sv[qb][4 * r + k] = x[k];
+      }
+      mq[qb][r] = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      asm volatile("" ::"v"(mq[qb][r]));
+    };
+    auto max_unit = [&](int qb) __attribute__((always_inline)) {
+      mx[qb] = xhalf_max(fmaxf(fmaxf(mq[qb][0], mq[qb][1]), fmaxf(mq[qb][2], mq[qb][3])));
+      asm volatile("" ::"v"(mx[qb]));
+    };
+
+#pragma unroll
+    for (int dc = 0; dc < KAHEAD && dc < C::NDC; ++dc) read_k(dc);
+#pragma unroll
+    for (int i = 0; i < NQK + NPV; ++i) {
+      if (i < NQK) {
+        const int dc = i / NQB, qb = i % NQB;
+        Sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[dc], qreg[qb][dc], dc == 0 ? (f32x16){} : Sn[qb], 0, 0, 0);
+        if (qb == NQB - 1 && dc + KAHEAD < C::NDC) read_k(dc + KAHEAD);
+        if (i >= VSLOT0) {
+          const int f = 2 * (i - VSLOT0);
+          if (f < NVF) read_v(f);
+          if (f + 1 < NVF) read_v(f + 1);
+        }
+#pragma unroll
+        for (int k = 0; k < E_PER; ++k)
+          if (i * E_PER + k < NE) exp_unit(i * E_PER + k);
+        if (i == NQK - 1) {
+#pragma unroll
+          for (int qb2 = 0; qb2 < NQB; ++qb2) {
+            Po[qb2][0] = __builtin_bit_cast(bf16x8, make_uint4(pk[qb2][0], pk[qb2][1], pk[qb2][2], pk[qb2][3]));
+            Po[qb2][1] = __builtin_bit_cast(bf16x8, make_uint4(pk[qb2][4], pk[qb2][5], pk[qb2][6], pk[qb2][7]));
+          }
+        }
+      } else {
+        const int m = i - NQK;
+        const int f = m / NQB, qb = m % NQB;  // V fragment f = half * NDB + db
+        if (do_pv)
+          oacc[f % C::NDB][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[f], Pi[qb][f / C::NDB],
+                                                                          oacc[f % C::NDB][qb], 0, 0, 0);
+        // S(j+1) copy: NT units from slot CS of this half on (the second, when
+        // there is room: one more matrix op between the last write and the
+        // first read); a query block's row max right after its 4 units.
+        constexpr int NT = 4 * NQB;
+        constexpr int CS = NPV > NT ? 1 : 0;
+        constexpr int T_PER = (NT + (NPV - CS) - 1) / (NPV - CS);
+#pragma unroll
+        for (int k = 0; k < T_PER; ++k) {
+          const int t = (m - CS) * T_PER + k;
+          if (m >= CS && t < NT) {
+            copy_unit(t);
+            if (t % 4 == 3) max_unit(t / 4);
+          }
+        }
+        if (m == (CS + (NT + T_PER - 1) / T_PER < NPV ? CS + (NT + T_PER - 1) / T_PER : NPV - 1)) dma();
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -426,36 +537,18 @@ __global__ __launch_bounds__(512 / NQB, 1) void chunk_attn_kernel(const AttnPara
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) pin_agpr(oacc[db][qb]);
-    row_ptrs(u + 2, kp, vp);
-    dma_cols(kp, kf);
     float alpha[NQB];
-    // sub-step 2u: S(2u) in SA, P(2u-1) in PB
+    // sub-step 2u: S(2u) in Sv, P(2u-1) in PB
     bool resc = prepare(2 * u, Sv, mx, alpha);
-    qk(ku, 1, SB);
-    softmax(Sv, PA);
-    if (!first) pv(vp_, 1, PB);
-    take_s(SB);
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      anchor(PA[qb][0]);
-      anchor(PA[qb][1]);
-      anchor(mx[qb]);
-    }
+    substep(ku, 1, SB, PA, vp_, 1, PB, !first, [&]() __attribute__((always_inline)) {
+      row_ptrs(u + 2, kp, vp);
+      dma_cols(kp, kf);
+    });
     if (resc) rescale_o(alpha);
     tile_barrier<2 * C::COLS_PER_WAVE>();
-    // sub-step 2u+1: S(2u+1) in SB, P(2u) in PA
-    dma_cols(vp, vp_);
+    // sub-step 2u+1: S(2u+1) in Sv, P(2u) in PA
     resc = prepare(2 * u + 1, Sv, mx, alpha);
-    qk(kn, 0, SA);
-    softmax(Sv, PB);
-    pv(vu, 0, PA);
-    take_s(SA);
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      anchor(PB[qb][0]);
-      anchor(PB[qb][1]);
-      anchor(mx[qb]);
-    }
+    substep(kn, 0, SA, PB, vu, 0, PA, true, [&]() __attribute__((always_inline)) { dma_cols(vp, vp_); });
     if (resc) rescale_o(alpha);
   };
   tile_steps(0, true, K0, K1, K2, V0, V2);
