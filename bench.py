@@ -215,11 +215,41 @@ def main():
     rope_q_mean, rope_host_us = timed(lambda: ring.rope3d(qs[0], C, y=q_rot), args.kernel_reps, attn)
     rope_k_mean, _ = timed(lambda: ring.rope3d(ks[0], C, y=k_rot), args.kernel_reps, attn)
     app_mean, app_host_us = timed(lambda: ring.append_evict(ks[-1], vs[-1], C), args.kernel_reps, attn)
+    # The same append with its inputs rotated over more than twice the
+    # 256 MB last-level cache (MALL), so every read comes from HBM.  In a
+    # rollout the committed K and V were produced just before the commit, so
+    # the figure above (inputs cache-warm) is the one a rollout sees.
+    n_cold = max(2, -(-(512 << 20) // (2 * ks[-1].numel() * 2)))
+    cold = [(randn(*ks[-1].shape), randn(*vs[-1].shape)) for _ in range(n_cold)]
+    cold_i = [0]
+
+    def app_cold():
+        kc, vc = cold[cold_i[0] % n_cold]
+        cold_i[0] += 1
+        ring.append_evict(kc, vc, C)
+
+    app_cold_mean, _ = timed(app_cold, max(args.kernel_reps, 2 * n_cold), attn)
+    del cold
+    # Reference: a plain elementwise copy (torch.neg) of the same bytes, its
+    # inputs rotated the same way -- what HBM delivers to a transfer this short.
+    copy_src = [randn(wl.append_bytes() // 4) for _ in range(n_cold)]
+    copy_dst = [torch.empty_like(x) for x in copy_src]
+    copy_i = [0]
+
+    def copy_cold():
+        a = copy_i[0] % n_cold
+        copy_i[0] += 1
+        torch.neg(copy_src[a], out=copy_dst[a])
+
+    copy_cold_mean, _ = timed(copy_cold, max(args.kernel_reps, 2 * n_cold), attn)
+    del copy_src, copy_dst
     torch.cuda.synchronize()
 
     attn_tflops = wl.attn_flops() / (attn_mean * 1e-3) / 1e12
     app_bytes = wl.append_bytes()
     app_gbs = app_bytes / (app_mean * 1e-3) / 1e9
+    app_cold_gbs = app_bytes / (app_cold_mean * 1e-3) / 1e9
+    copy_cold_gbs = app_bytes / (copy_cold_mean * 1e-3) / 1e9
     rope_bytes = 2 * wl.nq * wl.head_dim * 2 * (wl.n_q_heads + wl.n_kv_heads)
     rope_gbs = rope_bytes / ((rope_q_mean + rope_k_mean) * 1e-3) / 1e9
     prof_traffic = profiled_traffic(wl.name)
@@ -253,7 +283,10 @@ def main():
         "append": {"bound": "hbm", "achieved": round(app_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": round(app_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": app_bytes,
                    "traffic": profiled_traffic(wl.name, "append_traffic_bytes_per_launch"),
-                   "launch_ms_mean": round(app_mean, 5), "host_us_per_call": round(app_host_us, 1)},
+                   "launch_ms_mean": round(app_mean, 5), "host_us_per_call": round(app_host_us, 1),
+                   "achieved_inputs_from_hbm": round(app_cold_gbs, 1),
+                   "frac_inputs_from_hbm": round(app_cold_gbs / PEAK_HBM_GBS, 4),
+                   "copy_same_bytes_from_hbm": round(copy_cold_gbs, 1)},
         "rope": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
                  "launch_ms_mean_q": round(rope_q_mean, 5), "launch_ms_mean_k": round(rope_k_mean, 5),
