@@ -22,7 +22,8 @@ STATUS = {0: "WM_OK", 1: "WM_E_ARG", 2: "WM_E_SHAPE", 3: "WM_E_STATE", 4: "WM_E_
 
 # Every symbol include/wm.h declares.
 EXPORTS = ["wm_kvring_pool_bytes", "wm_kvring_create", "wm_kvring_destroy", "wm_kvring_reset",
-           "wm_kvring_view", "wm_rope3d", "wm_chunk_attn", "wm_chunk_attn_workspace_bytes",
+           "wm_kvring_view", "wm_rope3d", "wm_chunk_attn", "wm_chunk_attn_layer",
+           "wm_chunk_attn_workspace_bytes",
            "wm_kvring_append_evict", "wm_rollout_step", "wm_last_error"]
 
 
@@ -39,7 +40,7 @@ class Desc(ctypes.Structure):
                 ("frame_h", ctypes.c_int32), ("frame_w", ctypes.c_int32),
                 ("n_sink", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("max_chunk", ctypes.c_int32), ("rope_theta", ctypes.c_double),
-                ("rope_dims", ctypes.c_int32 * 3)]
+                ("rope_dims", ctypes.c_int32 * 3), ("n_layers", ctypes.c_int32)]
 
 
 class AppendReport(ctypes.Structure):
@@ -74,6 +75,7 @@ def lib():
         L.wm_kvring_view.argtypes = [vp, i32, P(RingView)]
         L.wm_rope3d.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp]
         L.wm_chunk_attn.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.c_float, vp, vp, sz, vp]
+        L.wm_chunk_attn_layer.argtypes = [vp, i32, vp, vp, vp, i32, vp, ctypes.c_float, vp, vp, sz, vp]
         L.wm_chunk_attn_workspace_bytes.argtypes = [vp, i32]
         L.wm_chunk_attn_workspace_bytes.restype = sz
         L.wm_kvring_append_evict.argtypes = [vp, vp, vp, i32, vp, vp, vp]
@@ -126,13 +128,15 @@ def _report_dict(r):
 
 
 class KVRing:
-    """One layer's bounded KV ring for ``batch`` independent rollouts."""
+    """A bounded KV ring for ``batch`` independent rollouts and ``n_layers``
+    attention layers that share its frames, slots and positions."""
 
     def __init__(self, batch, n_q_heads, n_kv_heads, head_dim, frame_h, frame_w, n_sink, window,
                  max_chunk, rope_theta=10000.0, rope_dims=(0, 0, 0), device="cuda",
-                 meta_only=False, pool=None):
+                 meta_only=False, pool=None, n_layers=1):
         self.desc = Desc(batch, n_q_heads, n_kv_heads, head_dim, frame_h, frame_w, n_sink, window,
-                         max_chunk, rope_theta, (ctypes.c_int32 * 3)(*rope_dims))
+                         max_chunk, rope_theta, (ctypes.c_int32 * 3)(*rope_dims), n_layers)
+        self.n_layers = max(1, n_layers)
         self.batch, self.hq, self.hkv, self.d = batch, n_q_heads, n_kv_heads, head_dim
         self.fh, self.fw, self.ft = frame_h, frame_w, frame_h * frame_w
         self.n_sink, self.window, self.max_chunk = n_sink, window, max_chunk
@@ -155,17 +159,18 @@ class KVRing:
                                           pool.numel(), ctypes.byref(self._h)))
 
     # -- pool views (tests and debugging) -----------------------------------
-    def _half(self, which):
+    def _half(self, which, layer):
         n = self.batch * self.slots * self.hkv * self.ft * self.d
         half = (n * 2 + 255) // 256 * 256
-        raw = self.pool[which * half: which * half + n * 2]
+        base = layer * 2 * half + which * half
+        raw = self.pool[base: base + n * 2]
         return raw.view(torch.bfloat16).view(self.batch, self.slots, self.hkv, self.ft, self.d)
 
-    def pool_k(self):
-        return self._half(0)
+    def pool_k(self, layer=0):
+        return self._half(0, layer)
 
-    def pool_v(self):
-        return self._half(1)
+    def pool_v(self, layer=0):
+        return self._half(1, layer)
 
     # -- C calls ---------------------------------------------------------------
     def close(self):
@@ -210,7 +215,7 @@ class KVRing:
         return lib().wm_chunk_attn_workspace_bytes(self._h, n_frames)
 
     def chunk_attn(self, q_rot, k_rot, v, n_frames, out=None, active=None, scale=0.0,
-                   workspace=None, stream=None):
+                   workspace=None, stream=None, layer=0):
         if out is None:
             out = torch.empty_like(q_rot)
         nq_el = self.tokens(n_frames, self.hq)
@@ -218,14 +223,16 @@ class KVRing:
         act_arr, act = _active(active, self.batch)
         ws = _ptr(workspace, "workspace", dtype=torch.uint8)
         ws_bytes = 0 if workspace is None else workspace.numel()
-        _check(lib().wm_chunk_attn(self._h, _ptr(q_rot, "q_rot", numel=nq_el),
-                                   _ptr(k_rot, "k_rot", numel=nk_el), _ptr(v, "v", numel=nk_el),
-                                   n_frames, act, float(scale), _ptr(out, "out", numel=nq_el),
-                                   ws, ws_bytes, _stream(stream)))
+        _check(lib().wm_chunk_attn_layer(self._h, layer, _ptr(q_rot, "q_rot", numel=nq_el),
+                                         _ptr(k_rot, "k_rot", numel=nk_el), _ptr(v, "v", numel=nk_el),
+                                         n_frames, act, float(scale), _ptr(out, "out", numel=nq_el),
+                                         ws, ws_bytes, _stream(stream)))
         return out
 
     def append_evict(self, k_raw, v, n_frames, active=None, stream=None):
-        nk_el = self.tokens(n_frames, self.hkv)
+        """k_raw, v: [B, n_frames*Ft, Hkv, d] per layer, stacked layer-major
+        ([L, B, ...]) for a multi-layer ring."""
+        nk_el = self.tokens(n_frames, self.hkv) * self.n_layers
         act_arr, act = _active(active, self.batch)
         if self.pool is None:                      # metadata-only ring: no device data
             kp = vp = None

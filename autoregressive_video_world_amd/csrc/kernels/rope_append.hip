@@ -114,9 +114,10 @@ __device__ __forceinline__ void pair_entry(const RopeParams& p, int row, int pr,
 }
 
 // grid: x = ceil(ft / tokens per block), y = row of p.rows,
-//       z = head group (rope) or 2 * head group + part (append: part 0 rotates
-//       K, part 1 copies V; separate waves, so the V stream runs while K waves
-//       compute).
+//       z = head group (rope) or 2 * (layer * head groups + head group) + part
+//       (append: part 0 rotates K, part 1 copies V -- separate waves, so the V
+//       stream runs while K waves compute; all layers of a multi-layer ring in
+//       one launch, each with its own input and pool slices).
 // Thread = (token, 16-byte slot c8 of the head dim); it handles kHeads heads of
 // that token, so its four pairs' table entries and its token's position are
 // looked up once.  A wave covers 64 / (d/8) consecutive tokens: each head's
@@ -130,8 +131,16 @@ __global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p)
   const uint32_t c8 = threadIdx.x & (kCpr - 1);
   const uint32_t tok = blockIdx.x * kTpb + (threadIdx.x >> kLgCpr);
   if (tok >= (uint32_t)p.ft) return;
-  const int hgroup = kAppend ? (int)(blockIdx.z >> 1) : (int)blockIdx.z;
+  int hgroup = kAppend ? (int)(blockIdx.z >> 1) : (int)blockIdx.z;
   const bool v_part = kAppend && (blockIdx.z & 1);
+  int64_t x_layer = 0, pool_layer = 0;
+  if constexpr (kAppend) {
+    const int n_hg = (p.n_heads + kHeads - 1) / kHeads;
+    const int layer = hgroup / n_hg;
+    hgroup -= layer * n_hg;
+    x_layer = (int64_t)layer * p.x_layer_stride;
+    pool_layer = (int64_t)layer * p.pool_layer_stride;
+  }
   const int h0 = hgroup * kHeads;
   const int nh = min(kHeads, p.n_heads - h0);
   const int rb = p.rows[row].b;
@@ -140,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p)
 
   // A frame of the chunk holds below 2^28 elements: 32-bit byte offsets.
   // Heads past the last are clamped on load; their stores are skipped.
-  const int64_t row_base = (int64_t)rb * p.x_b_stride + (int64_t)rj * p.ft * p.n_heads * (kCpr * 8);
+  const int64_t row_base = x_layer + (int64_t)rb * p.x_b_stride + (int64_t)rj * p.ft * p.n_heads * (kCpr * 8);
   const uint32_t src_off = ((tok * (uint32_t)p.n_heads + h0) * kCpr + c8) * 16u;
 
   // Destinations: the chunk layout (rope) or the slot's [head][token][d] block.
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p)
   uint32_t dst_off, dst_head;
   if constexpr (kAppend) {
     const int64_t slot_base =
-        ((int64_t)rb * p.ring_slots + p.rows[row].slot) * p.n_heads * p.ft * (kCpr * 8);
+        pool_layer + ((int64_t)rb * p.ring_slots + p.rows[row].slot) * p.n_heads * p.ft * (kCpr * 8);
     out = reinterpret_cast<char*>((v_part ? p.vdst : p.y) + slot_base);
     dst_head = (uint32_t)p.ft * head_bytes;
     dst_off = (uint32_t)h0 * dst_head + (tok * kCpr + c8) * 16u;
@@ -212,7 +221,7 @@ hipError_t launch_rows(const RopeParams& p, hipStream_t s) {
   const int lg = p.lg_cpr;
   const uint32_t tpb = kThreads >> lg;
   const dim3 grid((p.ft + tpb - 1) / tpb, p.n_rows,
-                  (kAppend ? 2 : 1) * ((p.n_heads + kHeads - 1) / kHeads));
+                  (kAppend ? 2 * p.n_layers : 1) * ((p.n_heads + kHeads - 1) / kHeads));
   if (lg == 4)
     hipLaunchKernelGGL((rope_rows_kernel<kAppend, 4>), grid, dim3(kThreads), 0, s, p);
   else

@@ -82,8 +82,15 @@ bool bands_of(const wm_kvring_desc& d, Bands* b) {
   return true;
 }
 
+constexpr int kMaxLayers = 256;
+
+// Layers of a descriptor (0 means one).
+int layers_of(const wm_kvring_desc& d) { return d.n_layers > 0 ? d.n_layers : 1; }
+
 struct Layout {
-  size_t k_off, v_off, tab_off;
+  size_t k_off, v_off;  // layer 0; layer l adds l * layer_bytes
+  size_t layer_bytes;
+  size_t tab_off;
   size_t hw;        // byte offset of the (cos, sin) table of the h then w band
   size_t tab_bytes, total;
 };
@@ -105,6 +112,8 @@ wm_status check_desc(const wm_kvring_desc* d, Bands* bands) {
                 WM_MAX_RING);
   if (d->max_chunk < 1 || d->max_chunk > WM_MAX_CHUNK)
     return fail(WM_E_SHAPE, "max_chunk %d not in [1, %d]", d->max_chunk, WM_MAX_CHUNK);
+  if (d->n_layers < 0 || d->n_layers > kMaxLayers)
+    return fail(WM_E_SHAPE, "n_layers %d not in [0, %d]", d->n_layers, kMaxLayers);
   if (!(d->rope_theta > 1.0) || !isfinite(d->rope_theta))
     return fail(WM_E_SHAPE, "rope_theta must be finite and > 1");
   if (!bands_of(*d, bands))
@@ -125,7 +134,8 @@ Layout layout_of(const wm_kvring_desc& d, const Bands& b) {
       (size_t)d.batch * (d.n_sink + d.window) * d.n_kv_heads * ft * d.head_dim * sizeof(uint16_t);
   L.k_off = 0;
   L.v_off = align_up(half, 256);
-  L.tab_off = align_up(L.v_off + half, 256);
+  L.layer_bytes = align_up(L.v_off + half, 256);
+  L.tab_off = L.layer_bytes * layers_of(d);
   const size_t entries = (size_t)d.frame_h * (b.dh / 2) + (size_t)d.frame_w * (b.dw / 2);
   L.hw = L.tab_off;
   // At least one entry: the kernels read entry 0 (unused) for t-band pairs.
@@ -143,7 +153,7 @@ struct wm_kvring {
   wm_kvring_desc desc;
   Bands bands;
   Layout L;
-  int ft, R;
+  int ft, R, n_layers;
   bool meta_only;
   uint8_t* pool;
   std::vector<int64_t> n_committed, t0;
@@ -311,6 +321,9 @@ wm_status do_append(wm_kvring* r, const wm_bf16* k_raw, const wm_bf16* v, int n_
     p.y = reinterpret_cast<uint16_t*>(r->pool + r->L.k_off);
     p.vdst = reinterpret_cast<uint16_t*>(r->pool + r->L.v_off);
     p.x_b_stride = (int64_t)n_frames * r->ft * r->desc.n_kv_heads * r->desc.head_dim;
+    p.n_layers = r->n_layers;
+    p.x_layer_stride = p.x_b_stride * B;
+    p.pool_layer_stride = (int64_t)(r->L.layer_bytes / sizeof(uint16_t));
     for (int b = 0; b < B; ++b) {
       if (!is_active(active, b)) continue;
       for (int j = 0; j < n_frames; ++j) {
@@ -398,17 +411,17 @@ int wg_per_bg_of(const wm_kvring* r, int n_frames) {
   return (group * task_blocks_of(r, n_frames) + waves - 1) / waves;
 }
 
-wm_status do_attn(const wm_kvring* r, const wm_bf16* q, const wm_bf16* kc, const wm_bf16* vc,
-                  int n_frames, const uint8_t* active, float scale, wm_bf16* out, void* ws,
-                  size_t ws_bytes, hipStream_t s) {
+wm_status do_attn(const wm_kvring* r, int layer, const wm_bf16* q, const wm_bf16* kc,
+                  const wm_bf16* vc, int n_frames, const uint8_t* active, float scale,
+                  wm_bf16* out, void* ws, size_t ws_bytes, hipStream_t s) {
   const wm_kvring_desc& d = r->desc;
   wm::AttnParams p;
   memset(&p, 0, sizeof p);
   p.q = q;
   p.kc = kc;
   p.vc = vc;
-  p.pk = reinterpret_cast<const uint16_t*>(r->pool + r->L.k_off);
-  p.pv = reinterpret_cast<const uint16_t*>(r->pool + r->L.v_off);
+  p.pk = reinterpret_cast<const uint16_t*>(r->pool + (size_t)layer * r->L.layer_bytes + r->L.k_off);
+  p.pv = reinterpret_cast<const uint16_t*>(r->pool + (size_t)layer * r->L.layer_bytes + r->L.v_off);
   p.out = out;
   p.hq = d.n_q_heads;
   p.hkv = d.n_kv_heads;
@@ -497,6 +510,7 @@ wm_status wm_kvring_create(const wm_kvring_desc* desc, void* dev_pool, size_t po
   r->L = L;
   r->ft = desc->frame_h * desc->frame_w;
   r->R = desc->n_sink + desc->window;
+  r->n_layers = layers_of(*desc);
   r->meta_only = meta;
   r->pool = static_cast<uint8_t*>(dev_pool);
   r->n_committed.assign(desc->batch, 0);
@@ -618,8 +632,18 @@ wm_status wm_chunk_attn(const wm_kvring* ring, const wm_bf16* q_rot, const wm_bf
                         const wm_bf16* v, int32_t n_frames, const uint8_t* active,
                         float softmax_scale, wm_bf16* out, void* workspace,
                         size_t workspace_bytes, void* stream) {
+  return wm_chunk_attn_layer(ring, 0, q_rot, k_rot, v, n_frames, active, softmax_scale, out,
+                             workspace, workspace_bytes, stream);
+}
+
+wm_status wm_chunk_attn_layer(const wm_kvring* ring, int32_t layer, const wm_bf16* q_rot,
+                              const wm_bf16* k_rot, const wm_bf16* v, int32_t n_frames,
+                              const uint8_t* active, float softmax_scale, wm_bf16* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   wm_status st;
   if ((st = check_ring(ring)) != WM_OK) return st;
+  if (layer < 0 || layer >= ring->n_layers)
+    return fail(WM_E_ARG, "layer %d not in [0, %d)", layer, ring->n_layers);
   if ((st = check_device_ring(ring)) != WM_OK) return st;
   if ((st = check_dev(q_rot, "q_rot")) != WM_OK) return st;
   if ((st = check_dev(k_rot, "k_rot")) != WM_OK) return st;
@@ -629,7 +653,7 @@ wm_status wm_chunk_attn(const wm_kvring* ring, const wm_bf16* q_rot, const wm_bf
   if (workspace && !aligned16(workspace)) return fail(WM_E_ARG, "workspace is not 16-byte aligned");
   if (!isfinite(softmax_scale)) return fail(WM_E_ARG, "softmax_scale is not finite");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = do_attn(ring, q_rot, k_rot, v, n_frames, active, softmax_scale, out, workspace,
+  st = do_attn(ring, layer, q_rot, k_rot, v, n_frames, active, softmax_scale, out, workspace,
                workspace_bytes, s);
   if (st != WM_OK) return st;
   return finish(s);
@@ -660,6 +684,9 @@ wm_status wm_rollout_step(wm_kvring* ring, int32_t n_denoise, const wm_bf16* con
   if ((st = check_ring(ring)) != WM_OK) return st;
   if ((st = check_device_ring(ring)) != WM_OK) return st;
   if ((st = check_frames(ring, n_frames)) != WM_OK) return st;
+  if (ring->n_layers != 1)
+    return fail(WM_E_UNSUPPORTED, "wm_rollout_step drives a one-layer ring (this one has %d layers)",
+                ring->n_layers);
   if (n_denoise < 1 || n_denoise > 64) return fail(WM_E_ARG, "n_denoise %d not in [1, 64]", n_denoise);
   if (!q || !k || !v || !out) return fail(WM_E_ARG, "q/k/v/out pointer arrays must not be NULL");
   for (int i = 0; i < n_denoise; ++i) {
@@ -678,7 +705,7 @@ wm_status wm_rollout_step(wm_kvring* ring, int32_t n_denoise, const wm_bf16* con
       return st;
     if ((st = do_rope(ring, k[i], k_rot_scratch, d.n_kv_heads, n_frames, nullptr, active, s)) != WM_OK)
       return st;
-    if ((st = do_attn(ring, q_rot_scratch, k_rot_scratch, v[i], n_frames, active, 0.f, out[i],
+    if ((st = do_attn(ring, 0, q_rot_scratch, k_rot_scratch, v[i], n_frames, active, 0.f, out[i],
                       workspace, workspace_bytes, s)) != WM_OK)
       return st;
   }

@@ -47,6 +47,9 @@ struct RopeParams {
   int32_t ring_slots;     // S + W (append)
   int32_t w_base;         // first entry of the w band in hw
   int32_t n_rows;
+  int32_t n_layers;       // append: layers written by one launch (rope: 1)
+  int64_t x_layer_stride;     // append: elements between layers of x / vsrc
+  int64_t pool_layer_stride;  // append: elements between layers of y / vdst
   FastDiv div_heads;      // division by n_heads
   FastDiv div_fw;         // division by frame width
   RopeRow rows[kRopeRows];

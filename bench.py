@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=12, help="q heads in the oracle sample")
+    ap.add_argument("--layers", type=int, default=30,
+                    help="layers of the multi-layer append measurement (0 = skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain elementwise copy of this many MiB first (untimed), as the "
                          "known-size reference for HBM byte counters")
@@ -243,6 +245,30 @@ def main():
 
     copy_cold_mean, _ = timed(copy_cold, max(args.kernel_reps, 2 * n_cold), attn)
     del copy_src, copy_dst
+
+    # A whole model's commit: the same workload's ring with `--layers` layers,
+    # every layer's K and V appended by one call (one launch), against the
+    # same bytes committed by one one-layer append per layer.  The inputs
+    # (layers x 28.8 MB at sf13b) exceed the last-level cache: HBM-bound.
+    layers = None
+    if args.layers > 1:
+        Ln = args.layers
+        mring = wm.KVRing(1, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                          wl.n_sink, wl.window, wl.chunk, device=dev, n_layers=Ln)
+        lk = randn(Ln, *ks[-1].shape)
+        lv = randn(Ln, *vs[-1].shape)
+        lay_mean, _ = timed(lambda: mring.append_evict(lk, lv, C), max(4, args.kernel_reps // 4), attn)
+        per_layer = lambda: [ring.append_evict(lk[i], lv[i], C) for i in range(Ln)]
+        per_mean, _ = timed(per_layer, max(2, args.kernel_reps // 10), attn)
+        lay_bytes = Ln * wl.append_bytes()
+        layers = {"bound": "hbm", "layers": Ln, "bytes_per_launch": lay_bytes,
+                  "achieved": round(lay_bytes / (lay_mean * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                  "unit": "GB/s", "frac": round(lay_bytes / (lay_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                  "launch_ms_mean": round(lay_mean, 4),
+                  "one_append_per_layer_gbs": round(lay_bytes / (per_mean * 1e-3) / 1e9, 1),
+                  "pool_bytes": mring.pool_bytes}
+        mring.close()
+        del lk, lv
     torch.cuda.synchronize()
 
     attn_tflops = wl.attn_flops() / (attn_mean * 1e-3) / 1e12
@@ -287,6 +313,7 @@ def main():
                    "achieved_inputs_from_hbm": round(app_cold_gbs, 1),
                    "frac_inputs_from_hbm": round(app_cold_gbs / PEAK_HBM_GBS, 4),
                    "copy_same_bytes_from_hbm": round(copy_cold_gbs, 1)},
+        "append_layers": layers,
         "rope": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
                  "launch_ms_mean_q": round(rope_q_mean, 5), "launch_ms_mean_k": round(rope_k_mean, 5),

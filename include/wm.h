@@ -88,6 +88,9 @@ typedef struct {
   double rope_theta;    /* RoPE base (e.g. 10000.0), > 1                              */
   int32_t rope_dims[3]; /* {d_t,d_h,d_w} even, sum d; {0,0,0} = default split:
                            d_h = d_w = 2*floor(d/6), d_t = d - d_h - d_w             */
+  int32_t n_layers;     /* L in [0, 256]: attention layers sharing the ring's frames,
+                           slots and positions (0 = 1).  Each layer has its own K/V
+                           in the pool; an append commits every layer at once     */
 } wm_kvring_desc;
 
 /* Per-rollout result of one append, in commit order.  A frame that is
@@ -118,10 +121,12 @@ typedef struct {
  * Pool
  *
  * Bytes of device memory a ring needs (0 if the descriptor is invalid).
- * Layout, all offsets from the pool base:
+ * Layout, all offsets from the pool base, per layer l = 0 .. L-1 at
+ * l * layer bytes (layer bytes = K half + V half, each rounded up to 256):
  *   K half : bf16 [B][S+W][Hkv][Ft][d]   -- each (slot, kv head) one
  *                                           contiguous Ft x d block
- *   V half : bf16 [B][S+W][Hkv][Ft][d]   -- at offset K-half bytes
+ *   V half : bf16 [B][S+W][Hkv][Ft][d]   -- after the K half (256-aligned)
+ * then, after the L layers, once:
  *   tables : (cos, sin) pairs of the h and w RoPE bands, [frame_h][d_h/2]
  *            then [frame_w][d_w/2]: fp64 copies of fp32-rounded values,
  *            256-byte aligned
@@ -198,6 +203,18 @@ wm_status wm_chunk_attn(const wm_kvring* ring, const wm_bf16* q_rot, const wm_bf
                         float softmax_scale, wm_bf16* out, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* wm_chunk_attn on layer `layer` (0 .. L-1) of a multi-layer ring: the same
+ * computation over that layer's committed K/V (wm_chunk_attn is layer 0).
+ * A whole model's cache then lives in one static pool whose size does not
+ * grow with the rollout (FlashDreams post, "Bounded Memory for Infinite
+ * Rollouts": per-rollout caches of fixed VRAM; Cosmos3-H-Dreams card,
+ * "Software Integration": static-shape KV cache).
+ * Errors: as wm_chunk_attn; WM_E_ARG for a layer out of range. */
+wm_status wm_chunk_attn_layer(const wm_kvring* ring, int32_t layer, const wm_bf16* q_rot,
+                              const wm_bf16* k_rot, const wm_bf16* v, int32_t n_frames,
+                              const uint8_t* active, float softmax_scale, wm_bf16* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes that let wm_chunk_attn split the key range for a chunk of
  * n_frames frames (0 if splitting never pays for this ring's shapes). */
 size_t wm_chunk_attn_workspace_bytes(const wm_kvring* ring, int32_t n_frames);
@@ -210,7 +227,9 @@ size_t wm_chunk_attn_workspace_bytes(const wm_kvring* ring, int32_t n_frames);
  * wm_rope3d at each frame's t and stored with V in the frame's slot; the
  * oldest window frames are evicted FIFO; sinks are never evicted.  Frames
  * that would be evicted again within the same append are not written.
- * k_raw, v : bf16 [B][n_frames*Ft][Hkv][d] (unrotated K).
+ * k_raw, v : bf16 [L][B][n_frames*Ft][Hkv][d] (unrotated K; L = the ring's
+ *            layers, layer-major): one bookkeeping step and one launch write
+ *            every layer's K and V into its own pool slice.
  * rep      : host array [B] or NULL; filled for active rollouts (inactive
  *            rollouts get n_written = n_evicted = 0).
  * Bookkeeping is host-side closed form: no device readback.  Stream order
@@ -232,7 +251,11 @@ wm_status wm_kvring_append_evict(wm_kvring* ring, const wm_bf16* k_raw, const wm
  * out[s]           : host array of n_denoise device output pointers.
  * workspace        : as for wm_chunk_attn.
  * rep              : as for wm_kvring_append_evict.
- * Errors: as the calls it makes; validation of everything happens first. */
+ * One-layer rings only (a model with L layers interleaves other work between
+ * its layers: it calls wm_rope3d / wm_chunk_attn_layer per layer and one
+ * wm_kvring_append_evict for all of them).
+ * Errors: as the calls it makes; WM_E_UNSUPPORTED for a multi-layer ring;
+ * validation of everything happens first. */
 wm_status wm_rollout_step(wm_kvring* ring, int32_t n_denoise, const wm_bf16* const* q,
                           const wm_bf16* const* k, const wm_bf16* const* v, int32_t n_frames,
                           const uint8_t* active, wm_bf16* q_rot_scratch, wm_bf16* k_rot_scratch,

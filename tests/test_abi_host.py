@@ -56,6 +56,51 @@ def test_pool_bytes_formula():
         r.close()
 
 
+def test_pool_bytes_of_layers():
+    """L layers: L copies of the K/V halves (each layer 256-aligned), then the
+    h/w tables once."""
+    for wl in WORKLOADS.values():
+        sizes = []
+        for L in (1, 2, 3, 7):
+            r = wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                          wl.n_sink, wl.window, wl.chunk, meta_only=True, n_layers=L)
+            sizes.append(r.pool_bytes)
+            r.close()
+        half = wl.batch * (wl.n_sink + wl.window) * wl.n_kv_heads * wl.ft * wl.head_dim * 2
+        layer = sizes[1] - sizes[0]
+        assert layer == 2 * ((half + 255) // 256 * 256)
+        assert sizes[2] - sizes[1] == layer and sizes[3] - sizes[2] == 4 * layer
+        zero = wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                         wl.n_sink, wl.window, wl.chunk, meta_only=True, n_layers=0)
+        assert zero.pool_bytes == sizes[0]   # 0 layers means one
+        zero.close()
+
+
+def test_multilayer_bookkeeping_is_shared():
+    """Appends on a metadata-only 5-layer ring report exactly what a one-layer
+    ring reports: layers share frames, slots and positions."""
+    one = wm.KVRing(2, 4, 2, 128, 4, 5, 1, 3, 2, meta_only=True)
+    five = wm.KVRing(2, 4, 2, 128, 4, 5, 1, 3, 2, meta_only=True, n_layers=5)
+    for i, n in enumerate([1, 2, 2, 1, 2, 2, 2]):
+        active = [True, i % 3 != 1]
+        assert one.append_evict(None, None, n, active=active) == five.append_evict(None, None, n, active=active)
+    assert [one.view(b) for b in range(2)] == [five.view(b) for b in range(2)]
+    one.close()
+    five.close()
+
+
+def test_layer_argument_is_checked_first():
+    L = wm.lib()
+    r = wm.KVRing(1, 2, 2, 64, 2, 2, 1, 1, 1, meta_only=True, n_layers=3)
+    p = ctypes.c_void_p(0x1000)
+    for layer in (-1, 3, 99):
+        assert L.wm_chunk_attn_layer(r._h, layer, p, p, p, 1, None, 0.0, p, None, 0, None) == 1
+        assert b"layer" in L.wm_last_error()
+    # a layer in range reaches the next check: the ring has no device pool
+    assert L.wm_chunk_attn_layer(r._h, 2, p, p, p, 1, None, 0.0, p, None, 0, None) == 3
+    r.close()
+
+
 def oracle_append(dq, n, t0):
     written, evicted = [], []
     for _ in range(n):
@@ -159,7 +204,7 @@ def make_desc(**kw):
                                  dict(max_chunk=17), dict(n_sink=200, window=57), dict(batch=0),
                                  dict(rope_dims=(42, 42, 42)), dict(rope_dims=(43, 43, 42)),
                                  dict(rope_theta=1.0), dict(frame_w=0), dict(window=-1),
-                                 dict(rope_dims=(128, 0, 0))])
+                                 dict(rope_dims=(128, 0, 0)), dict(n_layers=-1), dict(n_layers=257)])
 def test_invalid_descriptor(bad):
     L = wm.lib()
     d = make_desc(**bad)

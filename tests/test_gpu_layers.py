@@ -1,0 +1,140 @@
+"""GPU: a multi-layer ring (L attention layers sharing frames, slots and
+positions).
+
+Each layer gets its own seeded data and its own fp64 oracle.  Every chunk:
+per layer, RoPE of Q and K and wm_chunk_attn_layer (attention within the
+tolerance of tests/gpu_util.py, RoPE bit-exact); then one
+wm_kvring_append_evict with the layers' K and V stacked layer-major, which
+must leave every layer's slots bit-exact (K rotated at the frame's t, V
+copied) and every unplanned slot of every layer at the pool's sentinel.
+Rollouts are staggered so appends mix active and inactive rollouts.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import autoregressive_video_world_amd as wm
+from oracle.rollout import Rollout
+from wm_synth import Source, Workload
+from gpu_util import assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0xFFFF
+
+
+def W(cfg, **kw):
+    base = dict(cfg=cfg, name="layers%d" % cfg, batch=1, n_q_heads=2, n_kv_heads=2, head_dim=128,
+                frame_h=10, frame_w=10, chunk=1, n_sink=1, window=3, prefill=0, n_gen=6, n_denoise=1)
+    base.update(kw)
+    return Workload(**base)
+
+
+CASES = {
+    # several 64-key tiles and query blocks per layer, chunk of 2, window wraps
+    "mha_ft100_c2_L3": (W(201, chunk=2, n_gen=9, n_denoise=2), 3),
+    # d = 64, 3-frame chunks, ragged tails
+    "d64_ft50_c3_L2": (W(202, head_dim=64, frame_h=5, frame_w=10, chunk=3, window=4, n_gen=10), 2),
+    # GQA 8/2 with a prefill frame
+    "gqa_ft70_L3": (W(203, n_q_heads=8, n_kv_heads=2, frame_h=7, frame_w=10, window=2, prefill=1,
+                      n_gen=5), 3),
+    # three rollouts admitted two steps apart: appends with inactive rollouts
+    "batch3_staggered_L4": (W(204, batch=3, n_q_heads=4, n_kv_heads=4, frame_h=6, frame_w=7, window=2,
+                              prefill=1, n_gen=5, stagger=2), 4),
+}
+
+
+def make_ring(wl, L):
+    meta = wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                     wl.n_sink, wl.window, wl.chunk, meta_only=True, n_layers=L)
+    pool = torch.full((meta.pool_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    meta.close()
+    return wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                     wl.n_sink, wl.window, wl.chunk, pool=pool, n_layers=L)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_multilayer_rollout_parity(name):
+    wl, L = CASES[name]
+    print("case", name, flush=True)
+    B = wl.batch
+    srcs = [Source(dataclasses.replace(wl, cfg=wl.cfg * 100 + l)) for l in range(L)]
+    ring = make_ring(wl, L)
+    assert ring.pool_bytes > 0
+    oracles = [[Rollout(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                        wl.n_sink, wl.window) for _ in range(B)] for _ in range(L)]
+    actions = [([("prefill", wl.prefill)] if wl.prefill else []) + [("gen", c) for c in wl.chunks()]
+               for _ in range(B)]
+    used = [set() for _ in range(B)]
+    n_steps = max(wl.stagger * b + len(actions[b]) for b in range(B))
+    for g in range(n_steps):
+        groups = {}
+        for b in range(B):
+            k = g - wl.stagger * b
+            if 0 <= k < len(actions[b]):
+                groups.setdefault(actions[b][k], []).append(b)
+        for (kind, n), bs in sorted(groups.items()):
+            active = [b in bs for b in range(B)]
+            n0s = [oracles[0][b].n_committed if active[b] else None for b in range(B)]
+            k_last, v_last = [], []
+            for l in range(L):
+                if kind == "prefill":
+                    k_last.append(srcs[l].batch_chunk(n0s, n, -1, "k"))
+                    v_last.append(srcs[l].batch_chunk(n0s, n, -1, "v"))
+                    continue
+                for s in range(wl.n_denoise):
+                    q_np = srcs[l].batch_chunk(n0s, n, s, "q")
+                    k_np = srcs[l].batch_chunk(n0s, n, s, "k")
+                    v_np = srcs[l].batch_chunk(n0s, n, s, "v")
+                    q_rot = ring.rope3d(dev(q_np), n, active=active)
+                    k_rot = ring.rope3d(dev(k_np), n, active=active)
+                    out = ring.chunk_attn(q_rot, k_rot, dev(v_np), n, active=active, layer=l)
+                    qr, kr, o = host(q_rot), host(k_rot), host(out)
+                    for b in bs:
+                        ref_q, ref_k, ref_o = oracles[l][b].denoise_step(q_np[b], k_np[b], v_np[b], n)
+                        assert np.array_equal(qr[b], ref_q), ("q_rot", l, g, b, s)
+                        assert np.array_equal(kr[b], ref_k), ("k_rot", l, g, b, s)
+                        assert_close(o[b], ref_o, "layer %d step %d b %d s %d" % (l, g, b, s))
+                k_last.append(k_np)
+                v_last.append(v_np)
+            reps = ring.append_evict(dev(np.stack(k_last)), dev(np.stack(v_last)), n, active=active)
+            for b in range(B):
+                if not active[b]:
+                    assert reps[b] == {"written": [], "evicted": []}
+                    continue
+                for l in range(L):
+                    written, evicted = oracles[l][b].commit(k_last[l][b], v_last[l][b], n)
+                    assert reps[b] == {"written": written, "evicted": evicted}, (g, b, l)
+                used[b].update(s for f, s, t in oracles[0][b].retained())
+            for l in range(L):
+                pk, pv = host(ring.pool_k(l)), host(ring.pool_v(l))
+                for b in range(B):
+                    for f, slot, t in oracles[l][b].retained():
+                        kb, vb = oracles[l][b].cache[f]
+                        assert np.array_equal(pk[b, slot], kb.transpose(1, 0, 2)), ("K", l, b, f)
+                        assert np.array_equal(pv[b, slot], vb.transpose(1, 0, 2)), ("V", l, b, f)
+                    for slot in range(ring.slots):
+                        if slot not in used[b]:
+                            assert np.all(pk[b, slot] == SENTINEL) and np.all(pv[b, slot] == SENTINEL)
+    for b in range(B):
+        assert ring.view(b)["retained"] == oracles[0][b].retained()
+    ring.close()
+
+
+def test_multilayer_ring_rejects_what_it_does_not_support():
+    wl, L = CASES["mha_ft100_c2_L3"]
+    ring = make_ring(wl, L)
+    ft = wl.ft
+    q = torch.zeros(1, ft, wl.n_q_heads, wl.head_dim, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, ft, wl.n_kv_heads, wl.head_dim, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(wm.WMError) as e:
+        ring.chunk_attn(q, k, k, 1, layer=L)
+    assert e.value.name == "WM_E_ARG"
+    with pytest.raises(wm.WMError) as e:
+        ring.rollout_step([q], [k], [k], 1)
+    assert e.value.name == "WM_E_UNSUPPORTED"
+    assert ring.view(0)["n_committed"] == 0
+    ring.close()
