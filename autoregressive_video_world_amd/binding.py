@@ -40,7 +40,8 @@ class Desc(ctypes.Structure):
                 ("frame_h", ctypes.c_int32), ("frame_w", ctypes.c_int32),
                 ("n_sink", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("max_chunk", ctypes.c_int32), ("rope_theta", ctypes.c_double),
-                ("rope_dims", ctypes.c_int32 * 3), ("n_layers", ctypes.c_int32)]
+                ("rope_dims", ctypes.c_int32 * 3), ("n_layers", ctypes.c_int32),
+                ("n_views", ctypes.c_int32)]
 
 
 class AppendReport(ctypes.Structure):
@@ -133,12 +134,13 @@ class KVRing:
 
     def __init__(self, batch, n_q_heads, n_kv_heads, head_dim, frame_h, frame_w, n_sink, window,
                  max_chunk, rope_theta=10000.0, rope_dims=(0, 0, 0), device="cuda",
-                 meta_only=False, pool=None, n_layers=1):
+                 meta_only=False, pool=None, n_layers=1, n_views=1):
         self.desc = Desc(batch, n_q_heads, n_kv_heads, head_dim, frame_h, frame_w, n_sink, window,
-                         max_chunk, rope_theta, (ctypes.c_int32 * 3)(*rope_dims), n_layers)
+                         max_chunk, rope_theta, (ctypes.c_int32 * 3)(*rope_dims), n_layers, n_views)
         self.n_layers = max(1, n_layers)
+        self.n_views = max(1, n_views)
         self.batch, self.hq, self.hkv, self.d = batch, n_q_heads, n_kv_heads, head_dim
-        self.fh, self.fw, self.ft = frame_h, frame_w, frame_h * frame_w
+        self.fh, self.fw, self.ft = frame_h, frame_w, self.n_views * frame_h * frame_w
         self.n_sink, self.window, self.max_chunk = n_sink, window, max_chunk
         self.slots = n_sink + window
         # report buffer reused by every append (no per-call ctypes allocation)

@@ -179,9 +179,11 @@ __global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p)
     return;
   }
 
-  // Table entries first (L2 hits), then the K loads (HBM).
-  const uint32_t hpos = fast_div(tok, p.div_fw);
-  const uint32_t wpos = tok - hpos * p.fw;
+  // Table entries first (L2 hits), then the K loads (HBM).  Token index
+  // within the frame = view * (fh * fw) + h * fw + w.
+  const uint32_t rows = fast_div(tok, p.div_fw);
+  const uint32_t wpos = tok - rows * p.fw;
+  const uint32_t hpos = rows - fast_div(rows, p.div_fh) * p.fh;
   double c[4], s[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) pair_entry(p, row, (int)c8 * 4 + k, hpos, wpos, c[k], s[k]);

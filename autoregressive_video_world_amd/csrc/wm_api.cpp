@@ -83,6 +83,11 @@ bool bands_of(const wm_kvring_desc& d, Bands* b) {
 }
 
 constexpr int kMaxLayers = 256;
+constexpr int kMaxViews = 16;
+
+// Views per frame of a descriptor (0 means one) and tokens per stored frame.
+int views_of(const wm_kvring_desc& d) { return d.n_views > 0 ? d.n_views : 1; }
+int64_t ft_of(const wm_kvring_desc& d) { return (int64_t)views_of(d) * d.frame_h * d.frame_w; }
 
 // Layers of a descriptor (0 means one).
 int layers_of(const wm_kvring_desc& d) { return d.n_layers > 0 ? d.n_layers : 1; }
@@ -105,8 +110,11 @@ wm_status check_desc(const wm_kvring_desc* d, Bands* bands) {
   if (d->n_q_heads > 256) return fail(WM_E_SHAPE, "Hq=%d above 256", d->n_q_heads);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(WM_E_SHAPE, "head_dim %d: only 64 and 128 are built", d->head_dim);
-  if (d->frame_h < 1 || d->frame_w < 1 || (int64_t)d->frame_h * d->frame_w > (1 << 20))
-    return fail(WM_E_SHAPE, "frame grid %dx%d out of range", d->frame_h, d->frame_w);
+  if (d->n_views < 0 || d->n_views > kMaxViews)
+    return fail(WM_E_SHAPE, "n_views %d not in [0, %d]", d->n_views, kMaxViews);
+  if (d->frame_h < 1 || d->frame_w < 1 || ft_of(*d) > (1 << 20))
+    return fail(WM_E_SHAPE, "frame of %d views of %dx%d tokens out of range", views_of(*d), d->frame_h,
+                d->frame_w);
   if (d->n_sink < 0 || d->window < 0 || d->n_sink + d->window > WM_MAX_RING)
     return fail(WM_E_SHAPE, "sink %d + window %d must be in [0, %d]", d->n_sink, d->window,
                 WM_MAX_RING);
@@ -119,8 +127,8 @@ wm_status check_desc(const wm_kvring_desc* d, Bands* bands) {
   if (!bands_of(*d, bands))
     return fail(WM_E_SHAPE, "rope_dims {%d,%d,%d}: bands must be even, sum to d, d_t <= %d",
                 d->rope_dims[0], d->rope_dims[1], d->rope_dims[2], 2 * wm::kMaxTPairs);
-  const int64_t nq = (int64_t)d->max_chunk * d->frame_h * d->frame_w;
-  if ((int64_t)(d->n_sink + d->window + d->max_chunk) * d->frame_h * d->frame_w >= ((int64_t)1 << 24))
+  const int64_t nq = (int64_t)d->max_chunk * ft_of(*d);
+  if ((int64_t)(d->n_sink + d->window + d->max_chunk) * ft_of(*d) >= ((int64_t)1 << 24))
     return fail(WM_E_SHAPE, "visible keys (S+W+C)*Ft must stay below 2^24");
   if (nq * d->n_q_heads * d->head_dim > (int64_t)1 << 31)
     return fail(WM_E_SHAPE, "chunk tensor above 2^31 elements per rollout");
@@ -129,7 +137,7 @@ wm_status check_desc(const wm_kvring_desc* d, Bands* bands) {
 
 Layout layout_of(const wm_kvring_desc& d, const Bands& b) {
   Layout L;
-  const size_t ft = (size_t)d.frame_h * d.frame_w;
+  const size_t ft = (size_t)ft_of(d);
   const size_t half =
       (size_t)d.batch * (d.n_sink + d.window) * d.n_kv_heads * ft * d.head_dim * sizeof(uint16_t);
   L.k_off = 0;
@@ -217,6 +225,8 @@ void fill_tables_ptrs(const wm_kvring* r, wm::RopeParams* p, int n_heads) {
   p->row_vecs = r->ft * n_heads * (r->desc.head_dim / 8);
   p->div_heads = fast_div_of((uint32_t)n_heads);
   p->div_fw = fast_div_of((uint32_t)r->desc.frame_w);
+  p->div_fh = fast_div_of((uint32_t)r->desc.frame_h);
+  p->fh = r->desc.frame_h;
   p->ft = r->ft;
   p->fw = r->desc.frame_w;
   p->d = r->desc.head_dim;
@@ -377,7 +387,7 @@ int choose_split(int n_wg, int ntiles) {
   if (forced) return std::max(1, std::min(forced, ntiles));
   const double per_split = 400.0 / (64.0 * ntiles);
   int best = 1;
-  double best_cost = 1.0;
+  double best_cost = std::ceil((double)n_wg / kCUs);  // unsplit: whole rounds, no combine
   for (int s = 2; s <= kMaxSplit && ntiles >= 2 * s; ++s) {
     const double rounds = std::ceil((double)n_wg * s / kCUs);
     const double cost = rounds / s + per_split * s;
@@ -508,7 +518,7 @@ wm_status wm_kvring_create(const wm_kvring_desc* desc, void* dev_pool, size_t po
   r->desc = *desc;
   r->bands = bands;
   r->L = L;
-  r->ft = desc->frame_h * desc->frame_w;
+  r->ft = (int)ft_of(*desc);
   r->R = desc->n_sink + desc->window;
   r->n_layers = layers_of(*desc);
   r->meta_only = meta;

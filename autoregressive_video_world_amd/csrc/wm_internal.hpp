@@ -52,6 +52,8 @@ struct RopeParams {
   int64_t pool_layer_stride;  // append: elements between layers of y / vdst
   FastDiv div_heads;      // division by n_heads
   FastDiv div_fw;         // division by frame width
+  FastDiv div_fh;         // division by frame height (token -> row within its view)
+  int32_t fh;             // frame height (rows of one view)
   RopeRow rows[kRopeRows];
   float2 tcs[kRopeRows][kMaxTPairs];  // (cos, sin) of the t band at each row's t
 };

@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=12, help="q heads in the oracle sample")
     ap.add_argument("--layers", type=int, default=30,
                     help="layers of the multi-layer append measurement (0 = skip)")
+    ap.add_argument("--views-workload", type=int, default=6,
+                    help="multi-view workload whose steady-state attention is also timed (0 = skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain elementwise copy of this many MiB first (untimed), as the "
                          "known-size reference for HBM byte counters")
@@ -91,7 +93,8 @@ def cpu_baseline(wl, n_heads):
     from wm_synth import Source
 
     src = Source(wl)
-    ro = Rollout(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w, wl.n_sink, wl.window)
+    ro = Rollout(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w, wl.n_sink, wl.window,
+                 n_views=wl.n_views)
     for n0 in range(wl.n_sink + wl.window):
         ro.commit(src.chunk(0, n0, 1, -1, "k"), src.chunk(0, n0, 1, -1, "v"), 1)
     n = wl.chunk
@@ -152,7 +155,7 @@ def main():
         del a, b
 
     ring = wm.KVRing(1, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
-                     wl.n_sink, wl.window, wl.chunk, device=dev)
+                     wl.n_sink, wl.window, wl.chunk, device=dev, n_views=wl.n_views)
     C, D, ft = wl.chunk, wl.n_denoise, wl.ft
     # steady state: fill sinks + window (prefill-style appends of synthetic K/V)
     filled = 0
@@ -254,22 +257,53 @@ def main():
     if args.layers > 1:
         Ln = args.layers
         mring = wm.KVRing(1, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
-                          wl.n_sink, wl.window, wl.chunk, device=dev, n_layers=Ln)
+                          wl.n_sink, wl.window, wl.chunk, device=dev, n_layers=Ln, n_views=wl.n_views)
         lk = randn(Ln, *ks[-1].shape)
         lv = randn(Ln, *vs[-1].shape)
         lay_mean, _ = timed(lambda: mring.append_evict(lk, lv, C), max(4, args.kernel_reps // 4), attn)
         per_layer = lambda: [ring.append_evict(lk[i], lv[i], C) for i in range(Ln)]
         per_mean, _ = timed(per_layer, max(2, args.kernel_reps // 10), attn)
         lay_bytes = Ln * wl.append_bytes()
+        del lk, lv
+        csrc = randn(lay_bytes // 4)
+        cdst = torch.empty_like(csrc)
+        copy_mean, _ = timed(lambda: torch.neg(csrc, out=cdst), max(4, args.kernel_reps // 4), attn)
+        del csrc, cdst
         layers = {"bound": "hbm", "layers": Ln, "bytes_per_launch": lay_bytes,
                   "achieved": round(lay_bytes / (lay_mean * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                   "unit": "GB/s", "frac": round(lay_bytes / (lay_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                   "launch_ms_mean": round(lay_mean, 4),
                   "one_append_per_layer_gbs": round(lay_bytes / (per_mean * 1e-3) / 1e9, 1),
+                  "copy_same_bytes_gbs": round(lay_bytes / (copy_mean * 1e-3) / 1e9, 1),
                   "pool_bytes": mring.pool_bytes}
         mring.close()
-        del lk, lv
     torch.cuda.synchronize()
+
+    # Steady-state attention of a multi-view workload (several camera views
+    # per frame, attended jointly): same kernel, larger frames.
+    views = None
+    if args.views_workload and args.views_workload != args.workload:
+        vw = WORKLOADS[args.views_workload]
+        vring = wm.KVRing(1, vw.n_q_heads, vw.n_kv_heads, vw.head_dim, vw.frame_h, vw.frame_w,
+                          vw.n_sink, vw.window, vw.chunk, device=dev, n_views=vw.n_views)
+        for _ in range(vw.n_sink + vw.window):
+            vring.append_evict(randn(1, vw.ft, vw.n_kv_heads, vw.head_dim),
+                               randn(1, vw.ft, vw.n_kv_heads, vw.head_dim), 1)
+        vq = vring.rope3d(randn(1, vw.nq, vw.n_q_heads, vw.head_dim), vw.chunk)
+        vk = vring.rope3d(randn(1, vw.nq, vw.n_kv_heads, vw.head_dim), vw.chunk)
+        vv = randn(1, vw.nq, vw.n_kv_heads, vw.head_dim)
+        vo = torch.empty_like(vq)
+        vws_bytes = vring.workspace_bytes(vw.chunk)
+        vws = torch.empty(vws_bytes, dtype=torch.uint8, device=dev) if vws_bytes else None
+        v_mean, _ = timed(lambda: vring.chunk_attn(vq, vk, vv, vw.chunk, out=vo, workspace=vws), 3)
+        views = {"workload": "%s: %d q/%d kv heads, d %d, %d views of %dx%d tokens/frame (Nq %d, Nk %d)"
+                             % (vw.name, vw.n_q_heads, vw.n_kv_heads, vw.head_dim, vw.n_views, vw.frame_h,
+                                vw.frame_w, vw.nq, vw.steady_keys()),
+                 "attn_tflops": round(vw.attn_flops() / (v_mean * 1e-3) / 1e12, 2),
+                 "attn_pct_mfma_peak": round(100 * vw.attn_flops() / (v_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                 "launch_ms_mean": round(v_mean, 3)}
+        vring.close()
+        del vq, vk, vv, vo, vws
 
     attn_tflops = wl.attn_flops() / (attn_mean * 1e-3) / 1e12
     app_bytes = wl.append_bytes()
@@ -293,9 +327,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s: %d q/%d kv heads, d %d, %dx%d tokens/frame, chunk %d frames "
+        "config": {"workload": "%s: %d q/%d kv heads, d %d, %s%dx%d tokens/frame, chunk %d frames "
                                "(Nq %d), %d sink + %d window frames (Nk %d), %d denoise steps, steady state"
-                               % (wl.name, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h,
+                               % (wl.name, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                                  "%d views of " % wl.n_views if wl.n_views > 1 else "", wl.frame_h,
                                   wl.frame_w, C, wl.nq, wl.n_sink, wl.window, wl.steady_keys(), D),
                    "batch": 1, "n_q": wl.nq, "n_k": wl.steady_keys(), "denoise_steps": D},
         "denoise_steps_per_s_per_chunk": round(1e3 / (attn_mean + rope_q_mean + rope_k_mean), 2),
@@ -314,6 +349,7 @@ def main():
                    "frac_inputs_from_hbm": round(app_cold_gbs / PEAK_HBM_GBS, 4),
                    "copy_same_bytes_from_hbm": round(copy_cold_gbs, 1)},
         "append_layers": layers,
+        "views": views,
         "rope": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
                  "launch_ms_mean_q": round(rope_q_mean, 5), "launch_ms_mean_k": round(rope_k_mean, 5),

@@ -32,8 +32,9 @@
  *  - Every device pointer is a HIP device address, 16-byte aligned.
  *  - bf16 tensors are raw IEEE bfloat16 bit patterns (wm_bf16).
  *  - Token tensors are [B][n_frames*Ft][H][d] (row-major), token index =
- *    frame*Ft + h*frame_w + w, B = desc.batch (every rollout has a row block,
- *    active or not).
+ *    frame*Ft + view*frame_h*frame_w + h*frame_w + w (Ft = views * frame_h *
+ *    frame_w; one view unless the descriptor says more), B = desc.batch (every
+ *    rollout has a row block, active or not).
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every launch of a
  *    call goes onto that stream; no call synchronizes the device or copies
  *    device data to the host (wm_kvring_create aside).
@@ -80,8 +81,8 @@ typedef struct {
   int32_t n_q_heads;    /* Hq >= 1                                                    */
   int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0; q head h reads kv head h/(Hq/Hkv) */
   int32_t head_dim;     /* d: 64 or 128                                               */
-  int32_t frame_h;      /* latent grid height                                         */
-  int32_t frame_w;      /* latent grid width; Ft = frame_h*frame_w tokens per frame   */
+  int32_t frame_h;      /* latent grid height (of one view)                           */
+  int32_t frame_w;      /* latent grid width (of one view)                            */
   int32_t n_sink;       /* S >= 0: the first S frames of a sequence, never evicted    */
   int32_t window;       /* W >= 0: FIFO window of the most recent later frames        */
   int32_t max_chunk;    /* C in [1, WM_MAX_CHUNK]: frames per call                    */
@@ -91,6 +92,11 @@ typedef struct {
   int32_t n_layers;     /* L in [0, 256]: attention layers sharing the ring's frames,
                            slots and positions (0 = 1).  Each layer has its own K/V
                            in the pool; an append commits every layer at once     */
+  int32_t n_views;      /* V in [0, 16]: camera views per frame (0 = 1).  A frame is
+                           V grids of frame_h x frame_w tokens attended jointly;
+                           Ft = V*frame_h*frame_w (AlpaDreams write-up, VII and
+                           VIII: a four-view model, up to seven cameras, views
+                           attended together by one Transformer)                 */
 } wm_kvring_desc;
 
 /* Per-rollout result of one append, in commit order.  A frame that is
@@ -163,8 +169,10 @@ wm_status wm_kvring_view(const wm_kvring* ring, int32_t b, wm_ring_view* out);
  * 3D-RoPE of a chunk's Q or K (one denoise step).
  *
  * x, y : bf16 [B][n_frames*Ft][n_heads][d] (y may equal x).  Token r of chunk
- * frame j of rollout b sits at t = t_first[b] + j, h = (r mod Ft) / frame_w,
- * w = r mod frame_w; t_first == NULL means each rollout's next uncommitted
+ * frame j of rollout b sits at t = t_first[b] + j and, within its view,
+ * h = (r mod frame_h*frame_w) / frame_w, w = r mod frame_w (every view has
+ * its own grid; views of one frame share t); t_first == NULL means each
+ * rollout's next uncommitted
  * frame (t0 + n_committed).  Bands [t | h | w] of the head dim; in a band of
  * width d_a, pair j = elements (2j, 2j+1) rotated by angle pos*theta^(-2j/d_a);
  * cos/sin are libm fp64 values rounded once to fp32 (computed on the host);

@@ -29,10 +29,11 @@ from . import attention, bf16, ring, rope
 
 class Rollout:
     def __init__(self, n_q_heads, n_kv_heads, head_dim, frame_h, frame_w,
-                 n_sink, window, theta=10000.0, rope_dims=None, t0=0):
+                 n_sink, window, theta=10000.0, rope_dims=None, t0=0, n_views=1):
         self.Hq, self.Hkv, self.d = n_q_heads, n_kv_heads, head_dim
         self.fh, self.fw = frame_h, frame_w
-        self.ft = frame_h * frame_w
+        self.n_views = n_views
+        self.ft = n_views * frame_h * frame_w
         self.S, self.W = n_sink, window
         self.theta, self.rope_dims = theta, rope_dims
         self.ring = ring.DequeRing(n_sink, window)
@@ -57,7 +58,8 @@ class Rollout:
     def rope(self, x_bits, n_frames, t_first=None):
         if t_first is None:
             t_first = self.t_of(self.n_committed)
-        return rope.rotate_frames(x_bits, self.fh, self.fw, t_first, self.theta, self.rope_dims)
+        return rope.rotate_frames(x_bits, self.fh, self.fw, t_first, self.theta, self.rope_dims,
+                                  self.n_views)
 
     def keys_values(self, k_rot_chunk, v_chunk, n_frames):
         """Explicit concatenation of the visible frames' K_rot/V in temporal order."""

@@ -10,6 +10,13 @@ has a meaning:
 
 * positions: token r of the frame with id n in a sequence whose origin is t0
   sits at t = t0 + n, h = r // frame_w, w = r % frame_w;
+* several camera views (AlpaDreams write-up, sections VII-VIII: a four-view
+  model whose views one Transformer attends together) make a frame of
+  V * frame_h * frame_w tokens, view after view; each view keeps its own
+  (h, w) grid and all views of a frame share t: token r sits at
+  h = (r % (frame_h * frame_w)) // frame_w, w = r % frame_w (the pages say
+  nothing about encoding the view itself -- a learned view embedding would be
+  added outside this attention path);
 * the head dimension d is cut into three bands [t | h | w]; by default
   d_h = d_w = 2 * floor(d / 6) and d_t = d - d_h - d_w;
 * in a band of width d_a starting at element off_a, pair j (0 <= j < d_a/2)
@@ -64,12 +71,14 @@ def table_row(pos, theta, d_a, round_fp32=True):
     return c, s
 
 
-def token_positions(n_frames, frame_h, frame_w, t_first):
-    """(t, h, w) of every token of ``n_frames`` consecutive frames, token-major."""
-    ft = frame_h * frame_w
+def token_positions(n_frames, frame_h, frame_w, t_first, n_views=1):
+    """(t, h, w) of every token of ``n_frames`` consecutive frames, token-major;
+    a frame holds ``n_views`` views of frame_h x frame_w tokens."""
+    fv = frame_h * frame_w
+    ft = n_views * fv
     r = np.arange(n_frames * ft)
     t = t_first + r // ft
-    hw = r % ft
+    hw = (r % ft) % fv
     return t.astype(np.int64), (hw // frame_w).astype(np.int64), (hw % frame_w).astype(np.int64)
 
 
@@ -120,11 +129,11 @@ def rotate(x_bits, t, h, w, theta=10000.0, rope_dims=None):
     return bf16.f64_to_bits(rotate_f64(x, t, h, w, theta, rope_dims))
 
 
-def rotate_frames(x_bits, frame_h, frame_w, t_first, theta=10000.0, rope_dims=None):
+def rotate_frames(x_bits, frame_h, frame_w, t_first, theta=10000.0, rope_dims=None, n_views=1):
     """Rotate ``n_frames`` consecutive frames starting at absolute t ``t_first``."""
     T = x_bits.shape[0]
-    ft = frame_h * frame_w
+    ft = n_views * frame_h * frame_w
     if T % ft:
         raise ValueError("token count is not a whole number of frames")
-    t, h, w = token_positions(T // ft, frame_h, frame_w, t_first)
+    t, h, w = token_positions(T // ft, frame_h, frame_w, t_first, n_views)
     return rotate(x_bits, t, h, w, theta, rope_dims)

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol():
 
 def ring_for(wl, meta=True):
     return wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
-                     wl.n_sink, wl.window, wl.chunk, meta_only=meta)
+                     wl.n_sink, wl.window, wl.chunk, meta_only=meta, n_views=wl.n_views)
 
 
 def test_pool_bytes_formula():
@@ -56,6 +56,20 @@ def test_pool_bytes_formula():
         r.close()
 
 
+def test_pool_bytes_of_views():
+    """V views: every slot holds V grids of tokens, the h/w tables stay one
+    view's grid."""
+    one = wm.KVRing(1, 4, 2, 128, 6, 7, 1, 3, 2, meta_only=True)
+    for V in (2, 4, 7):
+        r = wm.KVRing(1, 4, 2, 128, 6, 7, 1, 3, 2, meta_only=True, n_views=V)
+        half1 = 4 * 2 * 42 * 128 * 2
+        tables = one.pool_bytes - 2 * ((half1 + 255) // 256 * 256)
+        assert r.pool_bytes == 2 * ((V * half1 + 255) // 256 * 256) + tables, V
+        assert r.ft == V * 42
+        r.close()
+    one.close()
+
+
 def test_pool_bytes_of_layers():
     """L layers: L copies of the K/V halves (each layer 256-aligned), then the
     h/w tables once."""
@@ -63,7 +77,7 @@ def test_pool_bytes_of_layers():
         sizes = []
         for L in (1, 2, 3, 7):
             r = wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
-                          wl.n_sink, wl.window, wl.chunk, meta_only=True, n_layers=L)
+                          wl.n_sink, wl.window, wl.chunk, meta_only=True, n_layers=L, n_views=wl.n_views)
             sizes.append(r.pool_bytes)
             r.close()
         half = wl.batch * (wl.n_sink + wl.window) * wl.n_kv_heads * wl.ft * wl.head_dim * 2
@@ -71,7 +85,7 @@ def test_pool_bytes_of_layers():
         assert layer == 2 * ((half + 255) // 256 * 256)
         assert sizes[2] - sizes[1] == layer and sizes[3] - sizes[2] == 4 * layer
         zero = wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
-                         wl.n_sink, wl.window, wl.chunk, meta_only=True, n_layers=0)
+                         wl.n_sink, wl.window, wl.chunk, meta_only=True, n_layers=0, n_views=wl.n_views)
         assert zero.pool_bytes == sizes[0]   # 0 layers means one
         zero.close()
 
@@ -204,7 +218,8 @@ def make_desc(**kw):
                                  dict(max_chunk=17), dict(n_sink=200, window=57), dict(batch=0),
                                  dict(rope_dims=(42, 42, 42)), dict(rope_dims=(43, 43, 42)),
                                  dict(rope_theta=1.0), dict(frame_w=0), dict(window=-1),
-                                 dict(rope_dims=(128, 0, 0)), dict(n_layers=-1), dict(n_layers=257)])
+                                 dict(rope_dims=(128, 0, 0)), dict(n_layers=-1), dict(n_layers=257),
+                                 dict(n_views=-1), dict(n_views=17)])
 def test_invalid_descriptor(bad):
     L = wm.lib()
     d = make_desc(**bad)

@@ -30,12 +30,13 @@ SENTINEL = 0xFFFF
 
 def make_ring(wl, t0s=None):
     pool_bytes = wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h,
-                           wl.frame_w, wl.n_sink, wl.window, wl.chunk, meta_only=True).pool_bytes
+                           wl.frame_w, wl.n_sink, wl.window, wl.chunk, meta_only=True,
+                           n_views=wl.n_views).pool_bytes
     pool = torch.full((pool_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
     ring = wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
-                     wl.n_sink, wl.window, wl.chunk, pool=pool)
+                     wl.n_sink, wl.window, wl.chunk, pool=pool, n_views=wl.n_views)
     oracles = [Rollout(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
-                       wl.n_sink, wl.window) for _ in range(wl.batch)]
+                       wl.n_sink, wl.window, n_views=wl.n_views) for _ in range(wl.batch)]
     if t0s:
         for b, t0 in enumerate(t0s):
             ring.reset(b, t0)
@@ -181,6 +182,11 @@ CASES = {
     "no_window": W(106, n_sink=2, window=0, frame_h=3, frame_w=11, chunk=2, n_gen=5),
     "chunk_gt_window": W(107, n_sink=1, window=2, chunk=4, frame_h=3, frame_w=5, n_gen=9),
     "gqa8_one_kv_head": W(108, n_q_heads=8, n_kv_heads=1, frame_h=9, frame_w=9, window=2, n_gen=4),
+    # camera views: each frame is several grids attended jointly, RoPE per view
+    "views3_c2": W(109, n_views=3, frame_h=4, frame_w=7, chunk=2, window=3, n_gen=7, n_denoise=2),
+    "views4_gqa_d64": W(110, n_views=4, head_dim=64, n_q_heads=6, n_kv_heads=2, frame_h=5, frame_w=6,
+                        window=2, prefill=1, n_gen=5),
+    "views7_batch2": W(111, n_views=7, batch=2, frame_h=3, frame_w=5, window=2, n_gen=5, stagger=1),
 }
 
 
@@ -197,7 +203,7 @@ def test_rollout_parity_split_keys(name):
     run_case(CASES[name], split=True)
 
 
-@pytest.mark.parametrize("name", ["mha_ft100_c2", "gqa_ft70", "d64_ft50_c3", "batch3_staggered",
+@pytest.mark.parametrize("name", ["mha_ft100_c2", "gqa_ft70", "d64_ft50_c3", "batch3_staggered", "views3_c2",
                                   "chunk_gt_window"])
 def test_rollout_parity_sharp_queries(name):
     """Q scaled x8: a peaked softmax (a dropped frame moves O by ~4e-2), and
@@ -210,7 +216,7 @@ def test_rollout_parity_absolute_origins():
     run_case(CASES["batch3_staggered"], t0s=[0, 1000, 9_999])
 
 
-@pytest.mark.parametrize("name", ["tiny", "batch3_staggered", "gqa_ft70"])
+@pytest.mark.parametrize("name", ["tiny", "batch3_staggered", "gqa_ft70", "views3_c2"])
 def test_rollout_step_parity(name):
     run_case(CASES[name], use_step=True)
     if name != "tiny":

@@ -161,3 +161,32 @@ def test_token_positions_layout():
     assert list(t) == [10] * 12 + [11] * 12
     assert list(h[:12]) == [0] * 4 + [1] * 4 + [2] * 4
     assert list(w[:5]) == [0, 1, 2, 3, 0]
+
+
+def test_token_positions_of_views_by_hand():
+    """Two frames of 3 views of a 2x3 grid: views share t, each restarts its grid."""
+    t, h, w = rope.token_positions(2, 2, 3, 5, n_views=3)
+    grid_h = [0, 0, 0, 1, 1, 1]
+    grid_w = [0, 1, 2, 0, 1, 2]
+    assert list(t) == [5] * 18 + [6] * 18
+    assert list(h) == grid_h * 6
+    assert list(w) == grid_w * 6
+
+
+def test_views_rotate_like_separate_single_view_frames():
+    """A V-view frame, rotated, equals each view's tokens rotated as a one-view
+    frame at the same t: views are independent grids that share the frame's t."""
+    rng = np.random.default_rng(7)
+    V, fh, fw, H, d = 4, 3, 5, 2, 64
+    x = rng.integers(0, 1 << 16, size=(2 * V * fh * fw, H, d), dtype=np.uint32).astype(np.uint16)
+    x[(x & 0x7F80) == 0x7F80] = 0x3F80          # no inf/NaN patterns
+    got = rope.rotate_frames(x, fh, fw, 123, n_views=V)
+    fv = fh * fw
+    for f in range(2):
+        for v in range(V):
+            sl = slice((f * V + v) * fv, (f * V + v + 1) * fv)
+            want = rope.rotate_frames(x[sl], fh, fw, 123 + f)
+            assert np.array_equal(got[sl], want), (f, v)
+    # and not like one tall grid: h of the second view does not continue the first's
+    t, h, w = rope.token_positions(1, fh, fw, 0, n_views=V)
+    assert h.max() == fh - 1

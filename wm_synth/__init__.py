@@ -19,6 +19,8 @@ drive  2B driving model (AlpaDreams write-up, section VIII:        16 heads, d 1
 mot15  15B MoT generation expert (Cosmos3-H-Dreams model card)     32 q / 8 kv heads, d 128, 30x40 tokens/frame,
                                                                    chunk 1, 1 reference + 17 window, 36 frames, 4 steps
 long   drive shapes, 8 rollouts admitted at staggered steps        10,000 frames each, 2 steps
+drv4v  drive shapes with four camera views per frame (AlpaDreams   16 heads, d 128, 4 views of 44x80 tokens,
+       write-up, VIII: four-view model)                            chunk 1, 1 sink + 3 window, 8 frames, 2 steps
 =====  =========================================================  ==========
 
 Draws: ``numpy.random.Generator(PCG64(SeedSequence([cfg, b, n, s + 1, kind])))``
@@ -56,10 +58,11 @@ class Workload:
     stagger: int = 0      # rollout b is admitted at global step stagger*b
     theta: float = 10000.0
     rope_dims: tuple = field(default=(0, 0, 0))
+    n_views: int = 1      # camera views per frame (each a frame_h x frame_w grid)
 
     @property
     def ft(self):
-        return self.frame_h * self.frame_w
+        return self.n_views * self.frame_h * self.frame_w
 
     @property
     def nq(self):
@@ -96,6 +99,7 @@ WORKLOADS = {
     3: Workload(3, "drive", 1, 16, 16, 128, 44, 80, 1, 1, 3, 1, 64, 2),
     4: Workload(4, "mot15", 1, 32, 8, 128, 30, 40, 1, 1, 17, 1, 36, 4),
     5: Workload(5, "long", 8, 16, 16, 128, 44, 80, 1, 1, 3, 1, 10000, 2, stagger=7),
+    6: Workload(6, "drv4v", 1, 16, 16, 128, 44, 80, 1, 1, 3, 1, 8, 2, n_views=4),
 }
 
 POOL_ENTRIES = 17
