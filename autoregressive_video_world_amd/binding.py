@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libwm.so")
 
 WM_MAX_CHUNK = 16
 WM_MAX_RING = 256
+EVICT_SLIDE = 0   # FIFO eviction of the oldest window frame
+EVICT_RESET = 1   # appends that would evict fail; the caller starts a new window
 
 STATUS = {0: "WM_OK", 1: "WM_E_ARG", 2: "WM_E_SHAPE", 3: "WM_E_STATE", 4: "WM_E_CAPACITY",
           5: "WM_E_HIP", 6: "WM_E_UNSUPPORTED"}
@@ -41,7 +43,7 @@ class Desc(ctypes.Structure):
                 ("n_sink", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("max_chunk", ctypes.c_int32), ("rope_theta", ctypes.c_double),
                 ("rope_dims", ctypes.c_int32 * 3), ("n_layers", ctypes.c_int32),
-                ("n_views", ctypes.c_int32)]
+                ("n_views", ctypes.c_int32), ("evict_policy", ctypes.c_int32)]
 
 
 class AppendReport(ctypes.Structure):
@@ -134,9 +136,10 @@ class KVRing:
 
     def __init__(self, batch, n_q_heads, n_kv_heads, head_dim, frame_h, frame_w, n_sink, window,
                  max_chunk, rope_theta=10000.0, rope_dims=(0, 0, 0), device="cuda",
-                 meta_only=False, pool=None, n_layers=1, n_views=1):
+                 meta_only=False, pool=None, n_layers=1, n_views=1, evict_policy=EVICT_SLIDE):
         self.desc = Desc(batch, n_q_heads, n_kv_heads, head_dim, frame_h, frame_w, n_sink, window,
-                         max_chunk, rope_theta, (ctypes.c_int32 * 3)(*rope_dims), n_layers, n_views)
+                         max_chunk, rope_theta, (ctypes.c_int32 * 3)(*rope_dims), n_layers, n_views,
+                         evict_policy)
         self.n_layers = max(1, n_layers)
         self.n_views = max(1, n_views)
         self.batch, self.hq, self.hkv, self.d = batch, n_q_heads, n_kv_heads, head_dim

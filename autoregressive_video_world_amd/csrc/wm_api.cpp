@@ -120,6 +120,9 @@ wm_status check_desc(const wm_kvring_desc* d, Bands* bands) {
                 WM_MAX_RING);
   if (d->max_chunk < 1 || d->max_chunk > WM_MAX_CHUNK)
     return fail(WM_E_SHAPE, "max_chunk %d not in [1, %d]", d->max_chunk, WM_MAX_CHUNK);
+  if (d->evict_policy != WM_EVICT_SLIDE && d->evict_policy != WM_EVICT_RESET)
+    return fail(WM_E_SHAPE, "evict_policy %d is neither WM_EVICT_SLIDE nor WM_EVICT_RESET",
+                d->evict_policy);
   if (d->n_layers < 0 || d->n_layers > kMaxLayers)
     return fail(WM_E_SHAPE, "n_layers %d not in [0, %d]", d->n_layers, kMaxLayers);
   if (!(d->rope_theta > 1.0) || !isfinite(d->rope_theta))
@@ -485,6 +488,19 @@ wm_status check_frames(const wm_kvring* r, int n_frames) {
   return WM_OK;
 }
 
+// WM_EVICT_RESET: every active rollout must hold n_frames more frames
+// without evicting (its sinks and window not yet full).
+wm_status check_room(const wm_kvring* r, int n_frames, const uint8_t* active) {
+  if (r->desc.evict_policy != WM_EVICT_RESET) return WM_OK;
+  for (int b = 0; b < r->desc.batch; ++b)
+    if (is_active(active, b) && r->n_committed[b] + n_frames > r->R)
+      return fail(WM_E_CAPACITY,
+                  "rollout %d holds %lld of %d frames: a %d-frame append would evict (reset policy: "
+                  "start a new window with wm_kvring_reset)",
+                  b, (long long)r->n_committed[b], r->R, n_frames);
+  return WM_OK;
+}
+
 wm_status check_device_ring(const wm_kvring* r) {
   if (r->meta_only) return fail(WM_E_STATE, "metadata-only ring has no device pool");
   return WM_OK;
@@ -679,6 +695,7 @@ wm_status wm_kvring_append_evict(wm_kvring* ring, const wm_bf16* k_raw, const wm
     if ((st = check_dev(k_raw, "k_raw")) != WM_OK) return st;
     if ((st = check_dev(v, "v")) != WM_OK) return st;
   }
+  if ((st = check_room(ring, n_frames, active)) != WM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = do_append(ring, k_raw, v, n_frames, active, rep, s)) != WM_OK) return st;
   if (ring->meta_only) return ok();
@@ -708,6 +725,7 @@ wm_status wm_rollout_step(wm_kvring* ring, int32_t n_denoise, const wm_bf16* con
   if ((st = check_dev(q_rot_scratch, "q_rot_scratch")) != WM_OK) return st;
   if ((st = check_dev(k_rot_scratch, "k_rot_scratch")) != WM_OK) return st;
   if (workspace && !aligned16(workspace)) return fail(WM_E_ARG, "workspace is not 16-byte aligned");
+  if ((st = check_room(ring, n_frames, active)) != WM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const wm_kvring_desc& d = ring->desc;
   for (int i = 0; i < n_denoise; ++i) {

@@ -63,6 +63,10 @@ extern "C" {
 #define WM_MAX_RING 256  /* sink + window slots per rollout                 */
 #define WM_MAX_BATCH 1024
 
+/* What an append does when a rollout's window is full (wm_kvring_desc.evict_policy). */
+#define WM_EVICT_SLIDE 0 /* evict the oldest window frame (FIFO); the default     */
+#define WM_EVICT_RESET 1 /* refuse: the caller starts a new window (reset)         */
+
 typedef uint16_t wm_bf16;
 typedef struct wm_kvring wm_kvring;
 
@@ -97,6 +101,10 @@ typedef struct {
                            Ft = V*frame_h*frame_w (AlpaDreams write-up, VII and
                            VIII: a four-view model, up to seven cameras, views
                            attended together by one Transformer)                 */
+  int32_t evict_policy; /* WM_EVICT_SLIDE or WM_EVICT_RESET (DreamZero page,
+                           "Sequential requests": at the local-attention window
+                           boundary the old KV is released, the frame position
+                           reset and a new window started)                         */
 } wm_kvring_desc;
 
 /* Per-rollout result of one append, in commit order.  A frame that is
@@ -240,11 +248,18 @@ size_t wm_chunk_attn_workspace_bytes(const wm_kvring* ring, int32_t n_frames);
  *            every layer's K and V into its own pool slice.
  * rep      : host array [B] or NULL; filled for active rollouts (inactive
  *            rollouts get n_written = n_evicted = 0).
+ * With evict_policy WM_EVICT_RESET an append that would evict a frame (or,
+ * with W == 0, commit one past the sinks) fails with WM_E_CAPACITY and
+ * changes nothing: the caller starts a new window with wm_kvring_reset (new
+ * origin, slots reused from 0) and prefills its conditioning again.
+ * Classifier-free guidance runs its branches as separate rollouts of the
+ * batch (each with its own cache); the guidance combine is outside this call.
  * Bookkeeping is host-side closed form: no device readback.  Stream order
  * matters: an append overwrites the slot of each frame it evicts, which the
  * chunk's own attention read, so it must follow that attention on the stream.
  * Prefill (conditioning frames committed without attention) is this call.
- * Errors: WM_E_ARG, WM_E_SHAPE, WM_E_HIP. */
+ * Errors: WM_E_ARG, WM_E_SHAPE, WM_E_CAPACITY (reset policy, window full),
+ * WM_E_HIP. */
 wm_status wm_kvring_append_evict(wm_kvring* ring, const wm_bf16* k_raw, const wm_bf16* v,
                                  int32_t n_frames, const uint8_t* active,
                                  wm_append_report* rep, void* stream);

@@ -219,7 +219,8 @@ def make_desc(**kw):
                                  dict(rope_dims=(42, 42, 42)), dict(rope_dims=(43, 43, 42)),
                                  dict(rope_theta=1.0), dict(frame_w=0), dict(window=-1),
                                  dict(rope_dims=(128, 0, 0)), dict(n_layers=-1), dict(n_layers=257),
-                                 dict(n_views=-1), dict(n_views=17)])
+                                 dict(n_views=-1), dict(n_views=17), dict(evict_policy=2),
+                                 dict(evict_policy=-1)])
 def test_invalid_descriptor(bad):
     L = wm.lib()
     d = make_desc(**bad)
@@ -281,3 +282,47 @@ def test_destroyed_handle_is_rejected():
     assert L.wm_kvring_view(h, 0, ctypes.byref(v)) == 3
     assert L.wm_kvring_append_evict(h, None, None, 1, None, None, None) == 3
     assert L.wm_kvring_destroy(None) == 1
+
+
+def test_reset_policy_refuses_to_evict_and_resets():
+    """WM_EVICT_RESET (DreamZero page, "Sequential requests": at the window
+    boundary the old KV is released, positions reset, a new window started):
+    an append that would evict fails with WM_E_CAPACITY and changes nothing;
+    after wm_kvring_reset the slots are reused from 0 at the new origin.  A
+    classifier-free-guidance pair is two rollouts that go through it together."""
+    S, W = 1, 3
+    r = wm.KVRing(2, 4, 2, 128, 4, 5, S, W, 2, meta_only=True, evict_policy=wm.EVICT_RESET)
+    reps = r.append_evict(None, None, 1)                 # conditioning (sink) of both branches
+    assert reps[0]["written"] == [(0, 0, 0)] and reps[1]["written"] == [(0, 0, 0)]
+    r.append_evict(None, None, 2)
+    reps = r.append_evict(None, None, 1)
+    assert reps[0] == {"written": [(3, 3, 3)], "evicted": []}
+    before = [r.view(b) for b in range(2)]
+    for n in (1, 2):
+        with pytest.raises(wm.WMError) as e:
+            r.append_evict(None, None, n)
+        assert e.value.name == "WM_E_CAPACITY"
+    with pytest.raises(wm.WMError) as e:                # one branch full is enough to refuse
+        r.append_evict(None, None, 1, active=[False, True])
+    assert [r.view(b) for b in range(2)] == before
+    for b in range(2):                                  # new window: positions restart
+        r.reset(b, 0)
+    reps = r.append_evict(None, None, 2)
+    assert reps[1] == {"written": [(0, 0, 0), (1, 1, 1)], "evicted": []}
+    assert r.view(1)["retained"] == [(0, 0, 0), (1, 1, 1)]
+    r.close()
+    # a slide ring of the same shape evicts instead
+    s = wm.KVRing(1, 4, 2, 128, 4, 5, S, W, 2, meta_only=True)
+    for n in (1, 2, 1):
+        s.append_evict(None, None, n)
+    assert s.append_evict(None, None, 1)[0] == {"written": [(4, 1, 4)], "evicted": [1]}
+    s.close()
+
+
+def test_reset_policy_with_no_window_stores_sinks_only():
+    r = wm.KVRing(1, 2, 2, 64, 2, 2, 2, 0, 2, meta_only=True, evict_policy=wm.EVICT_RESET)
+    r.append_evict(None, None, 2)
+    with pytest.raises(wm.WMError) as e:
+        r.append_evict(None, None, 1)
+    assert e.value.name == "WM_E_CAPACITY"
+    r.close()

@@ -1,0 +1,92 @@
+"""GPU: the reset-at-window-boundary policy with a classifier-free-guidance
+pair (DreamZero single-GPU page, "Sequential requests": at the
+local-attention window boundary the old KV is released, the frame position
+reset and a new window started; the scheduler runs CFG branches).
+
+Two rollouts (the conditional and unconditional branch, each with its own
+seeded data and cache) go through three windows: prefill of the
+conditioning frame, generated frames until the window is full, then a
+refused append (WM_E_CAPACITY, pool bytes unchanged), wm_kvring_reset at
+origin 0 and a fresh conditioning prefill.  RoPE and pool bytes are
+compared bit-exact and attention within tolerance against two fp64 oracles
+that do the same resets.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import autoregressive_video_world_amd as wm
+from oracle.rollout import Rollout
+from wm_synth import Source, Workload
+from gpu_util import assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("chunk", [1, 2])
+def test_reset_window_cfg_pair(chunk):
+    wl = Workload(301 + chunk, "reset_cfg", 2, 4, 2, 128, 6, 9, chunk, 1, 4, 1, 0, 2)
+    src = Source(wl)
+    B, S, W = 2, wl.n_sink, wl.window
+    meta = wm.KVRing(B, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w, S, W, chunk,
+                     meta_only=True, evict_policy=wm.EVICT_RESET)
+    pool = torch.zeros(meta.pool_bytes, dtype=torch.uint8, device="cuda")   # before create: the
+    meta.close()                                                            # tables live in the pool
+    ring = wm.KVRing(B, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w, S, W, chunk,
+                     evict_policy=wm.EVICT_RESET, pool=pool)
+    oracles = [Rollout(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w, S, W)
+               for _ in range(B)]
+    seq = 0   # data of each window differs: the frame index fed to the source keeps counting
+
+    def commit(k_np, v_np, n):
+        reps = ring.append_evict(dev(k_np), dev(v_np), n)
+        for b in range(B):
+            written, evicted = oracles[b].commit(k_np[b], v_np[b], n)
+            assert reps[b] == {"written": written, "evicted": evicted}
+            assert evicted == []
+
+    def check_pool():
+        pk, pv = host(ring.pool_k()), host(ring.pool_v())
+        for b in range(B):
+            for f, slot, t in oracles[b].retained():
+                kb, vb = oracles[b].cache[f]
+                assert np.array_equal(pk[b, slot], kb.transpose(1, 0, 2)), (b, f)
+                assert np.array_equal(pv[b, slot], vb.transpose(1, 0, 2)), (b, f)
+
+    for window in range(3):
+        # conditioning frame(s): prefill, no attention
+        n0s = [seq] * B
+        commit(src.batch_chunk(n0s, 1, -1, "k"), src.batch_chunk(n0s, 1, -1, "v"), 1)
+        seq += 1
+        while oracles[0].n_committed + chunk <= S + W:
+            n0s = [seq] * B
+            for s in range(wl.n_denoise):
+                q_np = src.batch_chunk(n0s, chunk, s, "q")
+                k_np = src.batch_chunk(n0s, chunk, s, "k")
+                v_np = src.batch_chunk(n0s, chunk, s, "v")
+                q_rot = ring.rope3d(dev(q_np), chunk)
+                k_rot = ring.rope3d(dev(k_np), chunk)
+                out = host(ring.chunk_attn(q_rot, k_rot, dev(v_np), chunk))
+                qr, kr = host(q_rot), host(k_rot)
+                for b in range(B):
+                    ref_q, ref_k, ref_o = oracles[b].denoise_step(q_np[b], k_np[b], v_np[b], chunk)
+                    assert np.array_equal(qr[b], ref_q) and np.array_equal(kr[b], ref_k)
+                    assert_close(out[b], ref_o, "window %d frame %d b %d s %d" % (window, seq, b, s))
+            commit(k_np, v_np, chunk)
+            check_pool()
+            seq += chunk
+        # the window is full: an append is refused and leaves every byte as it was
+        before = ring.pool.clone()
+        with pytest.raises(wm.WMError) as e:
+            ring.append_evict(dev(src.batch_chunk([seq] * B, chunk, -1, "k")),
+                              dev(src.batch_chunk([seq] * B, chunk, -1, "v")), chunk)
+        assert e.value.name == "WM_E_CAPACITY"
+        torch.cuda.synchronize()
+        assert torch.equal(before, ring.pool)
+        # new window: release, positions restart
+        for b in range(B):
+            ring.reset(b, 0)
+            oracles[b].reset(0)
+        assert ring.view(0)["retained"] == []
+    ring.close()
