@@ -5,4 +5,4 @@ kernels for gfx950 under ``csrc/``); ``binding`` marshals PyTorch tensors and
 streams into it.
 """
 
-from .binding import EVICT_RESET, EVICT_SLIDE, EXPORTS, KVRing, WMError, lib  # noqa: F401
+from .binding import EVICT_RESET, EVICT_SLIDE, EXPORTS, KVRing, RolloutGraph, WMError, lib  # noqa: F401

@@ -26,7 +26,8 @@ STATUS = {0: "WM_OK", 1: "WM_E_ARG", 2: "WM_E_SHAPE", 3: "WM_E_STATE", 4: "WM_E_
 EXPORTS = ["wm_kvring_pool_bytes", "wm_kvring_create", "wm_kvring_destroy", "wm_kvring_reset",
            "wm_kvring_view", "wm_rope3d", "wm_chunk_attn", "wm_chunk_attn_layer",
            "wm_chunk_attn_workspace_bytes",
-           "wm_kvring_append_evict", "wm_rollout_step", "wm_last_error"]
+           "wm_kvring_append_evict", "wm_rollout_step", "wm_rollout_graph_create",
+           "wm_rollout_graph_launch", "wm_rollout_graph_destroy", "wm_last_error"]
 
 
 class WMError(RuntimeError):
@@ -82,7 +83,10 @@ def lib():
         L.wm_chunk_attn_workspace_bytes.argtypes = [vp, i32]
         L.wm_chunk_attn_workspace_bytes.restype = sz
         L.wm_kvring_append_evict.argtypes = [vp, vp, vp, i32, vp, vp, vp]
-        L.wm_rollout_step.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.wm_rollout_step.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.wm_rollout_graph_create.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, P(vp)]
+        L.wm_rollout_graph_launch.argtypes = [vp, vp, P(i32), vp]
+        L.wm_rollout_graph_destroy.argtypes = [vp]
         L.wm_last_error.restype = ctypes.c_char_p
         for name in EXPORTS:
             if name not in ("wm_kvring_pool_bytes", "wm_chunk_attn_workspace_bytes", "wm_last_error"):
@@ -247,8 +251,7 @@ class KVRing:
                                             None if self.pool is None else _stream(stream)))
         return [_report_dict(r) for r in self._reps]
 
-    def rollout_step(self, qs, ks, vs, n_frames, outs=None, active=None, q_rot_scratch=None,
-                     k_rot_scratch=None, workspace=None, stream=None):
+    def _step_args(self, qs, ks, vs, n_frames, outs, active, q_rot_scratch, k_rot_scratch, workspace):
         D = len(qs)
         nq_el = self.tokens(n_frames, self.hq)
         nk_el = self.tokens(n_frames, self.hkv)
@@ -264,8 +267,56 @@ class KVRing:
         act_arr, act = _active(active, self.batch)
         ws = _ptr(workspace, "workspace", dtype=torch.uint8)
         ws_bytes = 0 if workspace is None else workspace.numel()
-        _check(lib().wm_rollout_step(self._h, D, qa, ka, va, n_frames, act,
-                                     _ptr(q_rot_scratch, "q_rot_scratch", numel=nq_el),
-                                     _ptr(k_rot_scratch, "k_rot_scratch", numel=nk_el),
-                                     oa, ws, ws_bytes, self._reps_ptr, _stream(stream)))
+        keep = (qa, ka, va, oa, act_arr, q_rot_scratch, k_rot_scratch, workspace, qs, ks, vs, outs)
+        args = (D, qa, ka, va, n_frames, act, _ptr(q_rot_scratch, "q_rot_scratch", numel=nq_el),
+                _ptr(k_rot_scratch, "k_rot_scratch", numel=nk_el), oa, ws, ws_bytes)
+        return outs, args, keep
+
+    def rollout_step(self, qs, ks, vs, n_frames, outs=None, active=None, q_rot_scratch=None,
+                     k_rot_scratch=None, workspace=None, stream=None, finalize_stream=None):
+        """n_denoise x (RoPE, attention), then the append; with finalize_stream
+        the append runs there, overlapping the next step's RoPE."""
+        outs, args, keep = self._step_args(qs, ks, vs, n_frames, outs, active, q_rot_scratch,
+                                           k_rot_scratch, workspace)
+        fs = None if finalize_stream is None else _stream(finalize_stream)
+        _check(lib().wm_rollout_step(self._h, *args, self._reps_ptr, _stream(stream), fs))
         return outs, [_report_dict(r) for r in self._reps]
+
+    def rollout_graph(self, qs, ks, vs, n_frames, outs=None, active=None, q_rot_scratch=None,
+                      k_rot_scratch=None, workspace=None):
+        """A HIP graph of one rollout step over these (fixed) buffers."""
+        return RolloutGraph(self, qs, ks, vs, n_frames, outs, active, q_rot_scratch, k_rot_scratch,
+                            workspace)
+
+
+class RolloutGraph:
+    """One rollout step as a HIP graph; launch() refreshes positions and slots
+    from the ring's bookkeeping and runs it (rebuilding it first when the
+    launch shapes have changed: see ``rebuilt``)."""
+
+    def __init__(self, ring, qs, ks, vs, n_frames, outs, active, q_rot_scratch, k_rot_scratch,
+                 workspace):
+        self.ring = ring
+        self.outs, args, self._keep = ring._step_args(qs, ks, vs, n_frames, outs, active, q_rot_scratch,
+                                                      k_rot_scratch, workspace)
+        self._h = ctypes.c_void_p()
+        _check(lib().wm_rollout_graph_create(ring._h, *args, ctypes.byref(self._h)))
+        self._rebuilt = ctypes.c_int32(0)
+        self.rebuilt = None
+
+    def launch(self, stream=None):
+        _check(lib().wm_rollout_graph_launch(self._h, self.ring._reps_ptr, ctypes.byref(self._rebuilt),
+                                             _stream(stream)))
+        self.rebuilt = bool(self._rebuilt.value)
+        return self.outs, [_report_dict(r) for r in self.ring._reps]
+
+    def close(self):
+        if self._h:
+            _check(lib().wm_rollout_graph_destroy(self._h))
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -657,27 +657,21 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
 
 }  // namespace
 
-hipError_t launch_chunk_attn(const AttnParams& p_in, int head_dim, hipStream_t s) {
-  AttnParams p = p_in;
+int chunk_attn_specs(AttnParams& p, int head_dim, LaunchSpec specs[2]) {
+  if (p.wave_qblocks != 2 || (head_dim != 128 && head_dim != 64)) return 0;
   p.n_wg = p.nb * p.hkv * p.wg_per_bg * p.nsplit;
   p.per_xcd = (p.n_wg + kXcds - 1) / kXcds;
-  const dim3 grid(p.per_xcd * kXcds);
-  if (p.wave_qblocks != 2) return hipErrorInvalidValue;
-  if (head_dim == 128)
-    hipLaunchKernelGGL((chunk_attn_kernel<128, 2>), grid, dim3(Cfg<128, 2>::THREADS), 0, s, p);
-  else
-    hipLaunchKernelGGL((chunk_attn_kernel<64, 2>), grid, dim3(Cfg<64, 2>::THREADS), 0, s, p);
-  if (p.nsplit > 1) {
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t threads = (int64_t)p.nb * p.nq * p.hq * (head_dim / 8);
-    const dim3 cgrid((unsigned)((threads + 255) / 256));
-    if (head_dim == 128)
-      hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(256), 0, s, p);
-  }
-  return hipGetLastError();
+  specs[0].grid = dim3(p.per_xcd * kXcds);
+  specs[0].block = dim3(Cfg<128, 2>::THREADS);
+  specs[0].func = head_dim == 128 ? reinterpret_cast<const void*>(&chunk_attn_kernel<128, 2>)
+                                  : reinterpret_cast<const void*>(&chunk_attn_kernel<64, 2>);
+  if (p.nsplit == 1) return 1;
+  const int64_t threads = (int64_t)p.nb * p.nq * p.hq * (head_dim / 8);
+  specs[1].grid = dim3((unsigned)((threads + 255) / 256));
+  specs[1].block = dim3(256);
+  specs[1].func = head_dim == 128 ? reinterpret_cast<const void*>(&attn_combine_kernel<128>)
+                                  : reinterpret_cast<const void*>(&attn_combine_kernel<64>);
+  return 2;
 }
 
 }  // namespace wm

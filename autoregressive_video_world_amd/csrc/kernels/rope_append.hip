@@ -219,22 +219,22 @@ __global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p)
 }
 
 template <bool kAppend>
-hipError_t launch_rows(const RopeParams& p, hipStream_t s) {
+LaunchSpec rows_spec(const RopeParams& p) {
   const int lg = p.lg_cpr;
   const uint32_t tpb = kThreads >> lg;
-  const dim3 grid((p.ft + tpb - 1) / tpb, p.n_rows,
-                  (kAppend ? 2 * p.n_layers : 1) * ((p.n_heads + kHeads - 1) / kHeads));
-  if (lg == 4)
-    hipLaunchKernelGGL((rope_rows_kernel<kAppend, 4>), grid, dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL((rope_rows_kernel<kAppend, 3>), grid, dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  LaunchSpec sp;
+  sp.grid = dim3((p.ft + tpb - 1) / tpb, p.n_rows,
+                 (kAppend ? 2 * p.n_layers : 1) * ((p.n_heads + kHeads - 1) / kHeads));
+  sp.block = dim3(kThreads);
+  sp.func = lg == 4 ? reinterpret_cast<const void*>(&rope_rows_kernel<kAppend, 4>)
+                    : reinterpret_cast<const void*>(&rope_rows_kernel<kAppend, 3>);
+  return sp;
 }
 
 }  // namespace
 
-hipError_t launch_rope3d(const RopeParams& p, hipStream_t s) { return launch_rows<false>(p, s); }
+LaunchSpec rope3d_spec(const RopeParams& p) { return rows_spec<false>(p); }
 
-hipError_t launch_kv_append(const RopeParams& p, hipStream_t s) { return launch_rows<true>(p, s); }
+LaunchSpec kv_append_spec(const RopeParams& p) { return rows_spec<true>(p); }
 
 }  // namespace wm

@@ -42,7 +42,8 @@ wm_status ok() {
 }
 
 std::mutex g_mu;
-std::set<const void*> g_live;
+std::set<const void*> g_live;    // live ring handles
+std::set<const void*> g_graphs;  // live rollout-graph handles
 
 bool sync_check_enabled() {
   static const bool on = [] {
@@ -176,6 +177,30 @@ struct wm_kvring {
     float2 cs[wm::kMaxTPairs];
   };
   mutable TRow t_cache[64];
+  // Overlapped finalize: ev_attn marks the last attention of a step on the
+  // main stream, ev_fin the append on the finalize stream; once an append has
+  // gone to a finalize stream, every later call that touches the pool waits
+  // for ev_fin first (RoPE, which does not, overlaps it).
+  hipEvent_t ev_attn = nullptr, ev_fin = nullptr;
+  bool fin_recorded = false;
+};
+
+struct wm_rollout_graph {
+  wm_kvring* ring;
+  int D, n_frames;
+  bool has_active;
+  std::vector<uint8_t> active;
+  std::vector<const wm_bf16*> q, k, v;
+  std::vector<wm_bf16*> out;
+  wm_bf16 *q_rot, *k_rot;
+  void* ws;
+  size_t ws_bytes;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipEvent_t ev_done = nullptr;  // after the last launch; waited on before the exec is dropped
+  bool launched = false;
+  std::vector<hipGraphNode_t> nodes;
+  std::vector<wm::LaunchSpec> shape;
 };
 
 namespace {
@@ -253,10 +278,69 @@ wm_status finish(hipStream_t s) {
   return ok();
 }
 
+// --- where the workers' launches go ---------------------------------------
+// A planned launch: its spec and the parameter struct it takes.
+struct PLaunch {
+  wm::LaunchSpec spec;
+  bool attn;             // parameters: ap (attention / combine) or rp (RoPE / append)
+  wm::RopeParams rp;
+  wm::AttnParams ap;
+  void* argv[1];
+  void* args() { return attn ? static_cast<void*>(&ap) : static_cast<void*>(&rp); }
+};
+
+// Kernel-node parameters of a planned launch (points into L: L must stay put
+// until the node is added or updated).
+hipKernelNodeParams node_params(PLaunch& L) {
+  hipKernelNodeParams kp;
+  memset(&kp, 0, sizeof kp);
+  L.argv[0] = L.args();
+  kp.func = const_cast<void*>(L.spec.func);
+  kp.gridDim = L.spec.grid;
+  kp.blockDim = L.spec.block;
+  kp.sharedMemBytes = 0;
+  kp.kernelParams = L.argv;
+  kp.extra = nullptr;
+  return kp;
+}
+
+// Launches on a stream, or records the launches (for a HIP graph) instead.
+struct Sink {
+  hipStream_t s = nullptr;
+  std::vector<PLaunch>* rec = nullptr;
+
+  hipError_t put(const wm::LaunchSpec& sp, const wm::RopeParams* rp, const wm::AttnParams* ap) {
+    if (rec) {
+      rec->emplace_back();
+      PLaunch& L = rec->back();
+      L.spec = sp;
+      L.attn = ap != nullptr;
+      if (rp) L.rp = *rp;
+      if (ap) L.ap = *ap;
+      return hipSuccess;
+    }
+    void* arg = ap ? (void*)ap : (void*)rp;
+    void* args[] = {arg};
+    return hipLaunchKernel(sp.func, sp.grid, sp.block, args, 0, s);
+  }
+  hipError_t rope(const wm::RopeParams& p) { return put(wm::rope3d_spec(p), &p, nullptr); }
+  hipError_t append(const wm::RopeParams& p) { return put(wm::kv_append_spec(p), &p, nullptr); }
+  hipError_t attn(wm::AttnParams p, int head_dim) {
+    wm::LaunchSpec sp[2];
+    const int n = wm::chunk_attn_specs(p, head_dim, sp);
+    if (n == 0) return hipErrorInvalidValue;
+    for (int i = 0; i < n; ++i) {
+      hipError_t e = put(sp[i], nullptr, &p);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+};
+
 // --- the unchecked workers (arguments validated by the callers) -----------
 
 wm_status do_rope(const wm_kvring* r, const wm_bf16* x, wm_bf16* y, int n_heads, int n_frames,
-                  const int64_t* t_first, const uint8_t* active, hipStream_t s) {
+                  const int64_t* t_first, const uint8_t* active, Sink& k) {
   wm::RopeParams p;
   memset(&p, 0, sizeof p);
   fill_tables_ptrs(r, &p, n_heads);
@@ -273,14 +357,14 @@ wm_status do_rope(const wm_kvring* r, const wm_bf16* x, wm_bf16* y, int n_heads,
       row.slot = -1;
       t_row(r, t0 + j, p.tcs[p.n_rows]);
       if (++p.n_rows == wm::kRopeRows) {
-        hipError_t e = wm::launch_rope3d(p, s);
+        hipError_t e = k.rope(p);
         if (e != hipSuccess) return hip_fail(e, "rope3d launch");
         p.n_rows = 0;
       }
     }
   }
   if (p.n_rows) {
-    hipError_t e = wm::launch_rope3d(p, s);
+    hipError_t e = k.rope(p);
     if (e != hipSuccess) return hip_fail(e, "rope3d launch");
   }
   return WM_OK;
@@ -316,8 +400,10 @@ void plan_append(const wm_kvring* r, int b, int n_frames, wm_append_report* rep,
   }
 }
 
+// Plans and launches (or records) one append; the bookkeeping advances only
+// when `commit` is set, after every launch was accepted.
 wm_status do_append(wm_kvring* r, const wm_bf16* k_raw, const wm_bf16* v, int n_frames,
-                    const uint8_t* active, wm_append_report* rep, hipStream_t s) {
+                    const uint8_t* active, wm_append_report* rep, Sink& k, bool commit = true) {
   const int B = r->desc.batch;
   std::vector<wm_append_report> reps(B);
   std::vector<Planned> plan((size_t)B * n_frames);
@@ -348,20 +434,21 @@ wm_status do_append(wm_kvring* r, const wm_bf16* k_raw, const wm_bf16* v, int n_
         row.slot = pl.slot;
         t_row(r, reps[b].t[j], p.tcs[p.n_rows]);
         if (++p.n_rows == wm::kRopeRows) {
-          hipError_t e = wm::launch_kv_append(p, s);
+          hipError_t e = k.append(p);
           if (e != hipSuccess) return hip_fail(e, "kv_append launch");
           p.n_rows = 0;
         }
       }
     }
     if (p.n_rows) {
-      hipError_t e = wm::launch_kv_append(p, s);
+      hipError_t e = k.append(p);
       if (e != hipSuccess) return hip_fail(e, "kv_append launch");
     }
   }
   // Commit only once every launch was accepted.
-  for (int b = 0; b < B; ++b)
-    if (is_active(active, b)) r->n_committed[b] += n_frames;
+  if (commit)
+    for (int b = 0; b < B; ++b)
+      if (is_active(active, b)) r->n_committed[b] += n_frames;
   if (rep) memcpy(rep, reps.data(), sizeof(wm_append_report) * B);
   return WM_OK;
 }
@@ -426,7 +513,7 @@ int wg_per_bg_of(const wm_kvring* r, int n_frames) {
 
 wm_status do_attn(const wm_kvring* r, int layer, const wm_bf16* q, const wm_bf16* kc,
                   const wm_bf16* vc, int n_frames, const uint8_t* active, float scale,
-                  wm_bf16* out, void* ws, size_t ws_bytes, hipStream_t s) {
+                  wm_bf16* out, void* ws, size_t ws_bytes, Sink& k) {
   const wm_kvring_desc& d = r->desc;
   wm::AttnParams p;
   memset(&p, 0, sizeof p);
@@ -460,7 +547,7 @@ wm_status do_attn(const wm_kvring* r, int layer, const wm_bf16* q, const wm_bf16
       p.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                            align_up(rows * d.head_dim * sizeof(float), 256));
     }
-    return wm::launch_chunk_attn(p, d.head_dim, s);
+    return k.attn(p, d.head_dim);
   };
   int max_ring = 0;
   for (int b = 0; b < d.batch; ++b) {
@@ -501,9 +588,112 @@ wm_status check_room(const wm_kvring* r, int n_frames, const uint8_t* active) {
   return WM_OK;
 }
 
+wm_status make_events(wm_kvring* r) {
+  hipError_t e = hipSuccess;
+  if (!r->ev_attn) e = hipEventCreateWithFlags(&r->ev_attn, hipEventDisableTiming);
+  if (e == hipSuccess && !r->ev_fin) e = hipEventCreateWithFlags(&r->ev_fin, hipEventDisableTiming);
+  return e == hipSuccess ? WM_OK : hip_fail(e, "event create");
+}
+
+// Order s after the last append that went to a finalize stream.
+wm_status wait_finalize(const wm_kvring* r, hipStream_t s) {
+  if (!r->fin_recorded) return WM_OK;
+  hipError_t e = hipStreamWaitEvent(s, r->ev_fin, 0);
+  return e == hipSuccess ? WM_OK : hip_fail(e, "finalize wait");
+}
+
 wm_status check_device_ring(const wm_kvring* r) {
   if (r->meta_only) return fail(WM_E_STATE, "metadata-only ring has no device pool");
   return WM_OK;
+}
+
+// Arguments of a rollout step (wm_rollout_step, wm_rollout_graph_create).
+wm_status check_step(const wm_kvring* ring, int n_denoise, const wm_bf16* const* q,
+                     const wm_bf16* const* k, const wm_bf16* const* v, int n_frames,
+                     const wm_bf16* q_rot, const wm_bf16* k_rot, wm_bf16* const* out,
+                     const void* workspace) {
+  wm_status st;
+  if ((st = check_ring(ring)) != WM_OK) return st;
+  if ((st = check_device_ring(ring)) != WM_OK) return st;
+  if ((st = check_frames(ring, n_frames)) != WM_OK) return st;
+  if (ring->n_layers != 1)
+    return fail(WM_E_UNSUPPORTED, "a rollout step drives a one-layer ring (this one has %d layers)",
+                ring->n_layers);
+  if (n_denoise < 1 || n_denoise > 64) return fail(WM_E_ARG, "n_denoise %d not in [1, 64]", n_denoise);
+  if (!q || !k || !v || !out) return fail(WM_E_ARG, "q/k/v/out pointer arrays must not be NULL");
+  for (int i = 0; i < n_denoise; ++i) {
+    if ((st = check_dev(q[i], "q[s]")) != WM_OK) return st;
+    if ((st = check_dev(k[i], "k[s]")) != WM_OK) return st;
+    if ((st = check_dev(v[i], "v[s]")) != WM_OK) return st;
+    if ((st = check_dev(out[i], "out[s]")) != WM_OK) return st;
+  }
+  if ((st = check_dev(q_rot, "q_rot_scratch")) != WM_OK) return st;
+  if ((st = check_dev(k_rot, "k_rot_scratch")) != WM_OK) return st;
+  if (workspace && !aligned16(workspace)) return fail(WM_E_ARG, "workspace is not 16-byte aligned");
+  return WM_OK;
+}
+
+// n_denoise x (RoPE of Q and K, attention), then, with `append`, the append
+// of the last step's K and V (bookkeeping advanced only with `commit`).  A
+// non-null wait_stream first orders the attentions after a pending finalize.
+wm_status do_step(wm_kvring* ring, int n_denoise, const wm_bf16* const* q, const wm_bf16* const* k,
+                  const wm_bf16* const* v, int n_frames, const uint8_t* active, wm_bf16* q_rot,
+                  wm_bf16* k_rot, wm_bf16* const* out, void* ws, size_t ws_bytes,
+                  wm_append_report* rep, Sink& sink, bool append, hipStream_t wait_stream,
+                  bool commit = true) {
+  wm_status st;
+  const wm_kvring_desc& d = ring->desc;
+  for (int i = 0; i < n_denoise; ++i) {
+    if ((st = do_rope(ring, q[i], q_rot, d.n_q_heads, n_frames, nullptr, active, sink)) != WM_OK)
+      return st;
+    if ((st = do_rope(ring, k[i], k_rot, d.n_kv_heads, n_frames, nullptr, active, sink)) != WM_OK)
+      return st;
+    if (i == 0 && wait_stream && (st = wait_finalize(ring, wait_stream)) != WM_OK) return st;
+    if ((st = do_attn(ring, 0, q_rot, k_rot, v[i], n_frames, active, 0.f, out[i], ws, ws_bytes,
+                      sink)) != WM_OK)
+      return st;
+  }
+  if (append)
+    return do_append(ring, k[n_denoise - 1], v[n_denoise - 1], n_frames, active, rep, sink, commit);
+  return WM_OK;
+}
+
+// The launches of one graph step for the ring's current state, recorded;
+// nothing is committed.  reps (host [B]) receives the append reports.
+wm_status plan_graph_step(wm_rollout_graph* g, std::vector<PLaunch>* plan, wm_append_report* reps) {
+  Sink rec;
+  rec.rec = plan;
+  plan->reserve(4 * g->D + 4);
+  return do_step(g->ring, g->D, g->q.data(), g->k.data(), g->v.data(), g->n_frames,
+                 g->has_active ? g->active.data() : nullptr, g->q_rot, g->k_rot, g->out.data(), g->ws,
+                 g->ws_bytes, reps, rec, true, nullptr, false);
+}
+
+// A graph of the planned launches in one dependency chain, and its instance.
+hipError_t build_graph(wm_rollout_graph* g, std::vector<PLaunch>& plan) {
+  hipError_t e = hipGraphCreate(&g->graph, 0);
+  for (size_t i = 0; e == hipSuccess && i < plan.size(); ++i) {
+    hipKernelNodeParams kp = node_params(plan[i]);
+    hipGraphNode_t node;
+    e = hipGraphAddKernelNode(&node, g->graph, i ? &g->nodes.back() : nullptr, i ? 1 : 0, &kp);
+    if (e == hipSuccess) {
+      g->nodes.push_back(node);
+      g->shape.push_back(plan[i].spec);
+    }
+  }
+  if (e == hipSuccess) e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+  return e;
+}
+
+void drop_graph(wm_rollout_graph* g) {
+  if (g->launched) hipEventSynchronize(g->ev_done);
+  g->launched = false;
+  if (g->exec) hipGraphExecDestroy(g->exec);
+  if (g->graph) hipGraphDestroy(g->graph);
+  g->exec = nullptr;
+  g->graph = nullptr;
+  g->nodes.clear();
+  g->shape.clear();
 }
 
 }  // namespace
@@ -578,6 +768,8 @@ wm_status wm_kvring_destroy(wm_kvring* ring) {
     std::lock_guard<std::mutex> lk(g_mu);
     g_live.erase(ring);
   }
+  if (ring->ev_attn) hipEventDestroy(ring->ev_attn);
+  if (ring->ev_fin) hipEventDestroy(ring->ev_fin);
   delete ring;
   return ok();
 }
@@ -634,7 +826,8 @@ wm_status wm_rope3d(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, int32_t
       if (is_active(active, b) && (t_first[b] < 0 || t_first[b] > ((int64_t)1 << 52)))
         return fail(WM_E_ARG, "t_first[%d] out of range [0, 2^52]", b);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = do_rope(ring, x, y, n_heads, n_frames, t_first, active, s)) != WM_OK) return st;
+  Sink k{s};
+  if ((st = do_rope(ring, x, y, n_heads, n_frames, t_first, active, k)) != WM_OK) return st;
   return finish(s);
 }
 
@@ -679,8 +872,10 @@ wm_status wm_chunk_attn_layer(const wm_kvring* ring, int32_t layer, const wm_bf1
   if (workspace && !aligned16(workspace)) return fail(WM_E_ARG, "workspace is not 16-byte aligned");
   if (!isfinite(softmax_scale)) return fail(WM_E_ARG, "softmax_scale is not finite");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = wait_finalize(ring, s)) != WM_OK) return st;
+  Sink k{s};
   st = do_attn(ring, layer, q_rot, k_rot, v, n_frames, active, softmax_scale, out, workspace,
-               workspace_bytes, s);
+               workspace_bytes, k);
   if (st != WM_OK) return st;
   return finish(s);
 }
@@ -697,7 +892,9 @@ wm_status wm_kvring_append_evict(wm_kvring* ring, const wm_bf16* k_raw, const wm
   }
   if ((st = check_room(ring, n_frames, active)) != WM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = do_append(ring, k_raw, v, n_frames, active, rep, s)) != WM_OK) return st;
+  if (!ring->meta_only && (st = wait_finalize(ring, s)) != WM_OK) return st;
+  Sink k{s};
+  if ((st = do_append(ring, k_raw, v, n_frames, active, rep, k)) != WM_OK) return st;
   if (ring->meta_only) return ok();
   return finish(s);
 }
@@ -706,40 +903,143 @@ wm_status wm_rollout_step(wm_kvring* ring, int32_t n_denoise, const wm_bf16* con
                           const wm_bf16* const* k, const wm_bf16* const* v, int32_t n_frames,
                           const uint8_t* active, wm_bf16* q_rot_scratch, wm_bf16* k_rot_scratch,
                           wm_bf16* const* out, void* workspace, size_t workspace_bytes,
-                          wm_append_report* rep, void* stream) {
+                          wm_append_report* rep, void* stream, void* finalize_stream) {
   wm_status st;
-  if ((st = check_ring(ring)) != WM_OK) return st;
-  if ((st = check_device_ring(ring)) != WM_OK) return st;
-  if ((st = check_frames(ring, n_frames)) != WM_OK) return st;
-  if (ring->n_layers != 1)
-    return fail(WM_E_UNSUPPORTED, "wm_rollout_step drives a one-layer ring (this one has %d layers)",
-                ring->n_layers);
-  if (n_denoise < 1 || n_denoise > 64) return fail(WM_E_ARG, "n_denoise %d not in [1, 64]", n_denoise);
-  if (!q || !k || !v || !out) return fail(WM_E_ARG, "q/k/v/out pointer arrays must not be NULL");
-  for (int i = 0; i < n_denoise; ++i) {
-    if ((st = check_dev(q[i], "q[s]")) != WM_OK) return st;
-    if ((st = check_dev(k[i], "k[s]")) != WM_OK) return st;
-    if ((st = check_dev(v[i], "v[s]")) != WM_OK) return st;
-    if ((st = check_dev(out[i], "out[s]")) != WM_OK) return st;
-  }
-  if ((st = check_dev(q_rot_scratch, "q_rot_scratch")) != WM_OK) return st;
-  if ((st = check_dev(k_rot_scratch, "k_rot_scratch")) != WM_OK) return st;
-  if (workspace && !aligned16(workspace)) return fail(WM_E_ARG, "workspace is not 16-byte aligned");
+  if ((st = check_step(ring, n_denoise, q, k, v, n_frames, q_rot_scratch, k_rot_scratch, out,
+                       workspace)) != WM_OK)
+    return st;
   if ((st = check_room(ring, n_frames, active)) != WM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const wm_kvring_desc& d = ring->desc;
-  for (int i = 0; i < n_denoise; ++i) {
-    if ((st = do_rope(ring, q[i], q_rot_scratch, d.n_q_heads, n_frames, nullptr, active, s)) != WM_OK)
-      return st;
-    if ((st = do_rope(ring, k[i], k_rot_scratch, d.n_kv_heads, n_frames, nullptr, active, s)) != WM_OK)
-      return st;
-    if ((st = do_attn(ring, 0, q_rot_scratch, k_rot_scratch, v[i], n_frames, active, 0.f, out[i],
-                      workspace, workspace_bytes, s)) != WM_OK)
-      return st;
+  hipStream_t fs = static_cast<hipStream_t>(finalize_stream);
+  Sink main{s};
+  if (!fs || fs == s) {
+    st = do_step(ring, n_denoise, q, k, v, n_frames, active, q_rot_scratch, k_rot_scratch, out,
+                 workspace, workspace_bytes, rep, main, true, s);
+    if (st != WM_OK) return st;
+    return finish(s);
   }
-  if ((st = do_append(ring, k[n_denoise - 1], v[n_denoise - 1], n_frames, active, rep, s)) != WM_OK)
+  // Overlapped finalize: the append waits only for this step's last
+  // attention (it overwrites the slots that attention read) and runs on the
+  // finalize stream; the next call's pool accesses wait for it.
+  if ((st = make_events(ring)) != WM_OK) return st;
+  st = do_step(ring, n_denoise, q, k, v, n_frames, active, q_rot_scratch, k_rot_scratch, out,
+               workspace, workspace_bytes, rep, main, false, s);
+  if (st != WM_OK) return st;
+  hipError_t e = hipEventRecord(ring->ev_attn, s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(fs, ring->ev_attn, 0);
+  if (e != hipSuccess) return hip_fail(e, "finalize ordering");
+  Sink fin{fs};
+  if ((st = do_append(ring, k[n_denoise - 1], v[n_denoise - 1], n_frames, active, rep, fin)) != WM_OK)
     return st;
+  e = hipEventRecord(ring->ev_fin, fs);
+  if (e != hipSuccess) return hip_fail(e, "finalize event");
+  ring->fin_recorded = true;
+  if ((st = finish(s)) != WM_OK) return st;
+  return finish(fs);
+}
+
+wm_status wm_rollout_graph_create(wm_kvring* ring, int32_t n_denoise, const wm_bf16* const* q,
+                                  const wm_bf16* const* k, const wm_bf16* const* v,
+                                  int32_t n_frames, const uint8_t* active, wm_bf16* q_rot_scratch,
+                                  wm_bf16* k_rot_scratch, wm_bf16* const* out, void* workspace,
+                                  size_t workspace_bytes, wm_rollout_graph** graph_out) {
+  wm_status st;
+  if (!graph_out) return fail(WM_E_ARG, "graph_out is NULL");
+  if ((st = check_step(ring, n_denoise, q, k, v, n_frames, q_rot_scratch, k_rot_scratch, out,
+                       workspace)) != WM_OK)
+    return st;
+  wm_rollout_graph* g = new wm_rollout_graph();
+  g->ring = ring;
+  g->D = n_denoise;
+  g->n_frames = n_frames;
+  g->has_active = active != nullptr;
+  if (active) g->active.assign(active, active + ring->desc.batch);
+  g->q.assign(q, q + n_denoise);
+  g->k.assign(k, k + n_denoise);
+  g->v.assign(v, v + n_denoise);
+  g->out.assign(out, out + n_denoise);
+  g->q_rot = q_rot_scratch;
+  g->k_rot = k_rot_scratch;
+  g->ws = workspace;
+  g->ws_bytes = workspace_bytes;
+  // The launches of one step for the ring as it is now (nothing committed).
+  std::vector<PLaunch> plan;
+  if ((st = plan_graph_step(g, &plan, nullptr)) != WM_OK) {
+    delete g;
+    return st;
+  }
+  hipError_t e = hipEventCreateWithFlags(&g->ev_done, hipEventDisableTiming);
+  if (e == hipSuccess) e = build_graph(g, plan);
+  if (e != hipSuccess) {
+    drop_graph(g);
+    if (g->ev_done) hipEventDestroy(g->ev_done);
+    delete g;
+    return hip_fail(e, "graph build");
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_graphs.insert(g);
+  }
+  *graph_out = g;
+  return ok();
+}
+
+wm_status wm_rollout_graph_launch(wm_rollout_graph* g, wm_append_report* rep, int32_t* rebuilt,
+                                  void* stream) {
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g || !g_graphs.count(g)) return fail(WM_E_STATE, "graph handle is not live");
+  }
+  wm_status st;
+  wm_kvring* ring = g->ring;
+  if ((st = check_ring(ring)) != WM_OK) return st;
+  const uint8_t* active = g->has_active ? g->active.data() : nullptr;
+  if ((st = check_room(ring, g->n_frames, active)) != WM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<PLaunch> plan;
+  std::vector<wm_append_report> reps(ring->desc.batch);
+  if ((st = plan_graph_step(g, &plan, reps.data())) != WM_OK) return st;
+  bool same = plan.size() == g->shape.size();
+  for (size_t i = 0; same && i < plan.size(); ++i) {
+    const wm::LaunchSpec &a = plan[i].spec, &b = g->shape[i];
+    same = a.func == b.func && a.grid.x == b.grid.x && a.grid.y == b.grid.y && a.grid.z == b.grid.z &&
+           a.block.x == b.block.x;
+  }
+  if ((st = wait_finalize(ring, s)) != WM_OK) return st;
+  hipError_t e = hipSuccess;
+  if (same) {
+    for (size_t i = 0; e == hipSuccess && i < plan.size(); ++i) {
+      hipKernelNodeParams kp = node_params(plan[i]);
+      e = hipGraphExecKernelNodeSetParams(g->exec, g->nodes[i], &kp);
+    }
+  } else {
+    // New launch shapes (the window filling, a different key split): a new
+    // graph of this step's launches replaces the old one.
+    drop_graph(g);
+    e = build_graph(g, plan);
+    if (e != hipSuccess) drop_graph(g);
+  }
+  if (e == hipSuccess) e = hipGraphLaunch(g->exec, s);
+  if (e == hipSuccess) e = hipEventRecord(g->ev_done, s);
+  if (e != hipSuccess) return hip_fail(e, "graph launch");
+  g->launched = true;
+  for (int b = 0; b < ring->desc.batch; ++b)
+    if (is_active(active, b)) ring->n_committed[b] += g->n_frames;
+  if (rep) memcpy(rep, reps.data(), sizeof(wm_append_report) * ring->desc.batch);
+  if (rebuilt) *rebuilt = same ? 0 : 1;
   return finish(s);
+}
+
+wm_status wm_rollout_graph_destroy(wm_rollout_graph* g) {
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g || !g_graphs.count(g)) return fail(WM_E_STATE, "graph handle is not live");
+    g_graphs.erase(g);
+  }
+  drop_graph(g);
+  hipEventDestroy(g->ev_done);
+  delete g;
+  return ok();
 }
 
 const char* wm_last_error(void) { return g_err.c_str(); }

@@ -58,8 +58,17 @@ struct RopeParams {
   float2 tcs[kRopeRows][kMaxTPairs];  // (cos, sin) of the t band at each row's t
 };
 
-hipError_t launch_rope3d(const RopeParams& p, hipStream_t s);
-hipError_t launch_kv_append(const RopeParams& p, hipStream_t s);
+// One kernel launch of the library: kernel, grid and block.  Every kernel
+// takes a single parameter struct by value; the host runtime launches a spec
+// directly (hipLaunchKernel) or makes it a node of a HIP graph.
+struct LaunchSpec {
+  const void* func;
+  dim3 grid;
+  dim3 block;
+};
+
+LaunchSpec rope3d_spec(const RopeParams& p);
+LaunchSpec kv_append_spec(const RopeParams& p);
 
 // ---------------------------------------------------------------------------
 // Chunk attention
@@ -91,6 +100,9 @@ struct AttnParams {
   int32_t n_ring[kAttnMaxB];   // visible ring frames (slots 0 .. n_ring-1)
 };
 
-hipError_t launch_chunk_attn(const AttnParams& p, int head_dim, hipStream_t s);
+// Launches of one attention group: fills p's derived fields (workgroup count,
+// XCD stride) and returns the attention launch and, when the key range is
+// split, the combine launch (both take p); 0 if the shape is not built.
+int chunk_attn_specs(AttnParams& p, int head_dim, LaunchSpec specs[2]);
 
 }  // namespace wm

@@ -69,6 +69,7 @@ extern "C" {
 
 typedef uint16_t wm_bf16;
 typedef struct wm_kvring wm_kvring;
+typedef struct wm_rollout_graph wm_rollout_graph;
 
 typedef enum {
   WM_OK = 0,
@@ -274,6 +275,13 @@ wm_status wm_kvring_append_evict(wm_kvring* ring, const wm_bf16* k_raw, const wm
  * out[s]           : host array of n_denoise device output pointers.
  * workspace        : as for wm_chunk_attn.
  * rep              : as for wm_kvring_append_evict.
+ * finalize_stream  : NULL (or `stream`) = everything on `stream`.  Otherwise
+ *                    the append (FlashDreams post, "Hot-Path Generation,
+ *                    Background State Updates": finalize() off the critical
+ *                    path) goes to finalize_stream, ordered after this step's
+ *                    last attention only; every later call on the ring that
+ *                    reads or writes the pool waits for it, so the next
+ *                    step's RoPE overlaps it.
  * One-layer rings only (a model with L layers interleaves other work between
  * its layers: it calls wm_rope3d / wm_chunk_attn_layer per layer and one
  * wm_kvring_append_evict for all of them).
@@ -283,7 +291,37 @@ wm_status wm_rollout_step(wm_kvring* ring, int32_t n_denoise, const wm_bf16* con
                           const wm_bf16* const* k, const wm_bf16* const* v, int32_t n_frames,
                           const uint8_t* active, wm_bf16* q_rot_scratch, wm_bf16* k_rot_scratch,
                           wm_bf16* const* out, void* workspace, size_t workspace_bytes,
-                          wm_append_report* rep, void* stream);
+                          wm_append_report* rep, void* stream, void* finalize_stream);
+
+/* ---------------------------------------------------------------------------
+ * One rollout step as a HIP graph (Cosmos-H-Dreams news item: inference with
+ * compilation and CUDA Graphs; Cosmos3-H-Dreams card, "Software
+ * Integration": static shapes).
+ *
+ * wm_rollout_graph_create builds a graph of the launches wm_rollout_step
+ * would make for these buffers (fixed for the graph's life) and this active
+ * set, from the ring as it is now; it changes nothing.  The graph holds only
+ * kernel nodes, in one dependency chain.
+ * wm_rollout_graph_launch runs one step: it plans the step from the ring's
+ * bookkeeping (positions, slots, visible frames), writes those parameters
+ * into the graph's nodes and launches the graph on `stream`, then commits
+ * the append like wm_kvring_append_evict.  When the planned launches differ
+ * in kernel or grid from the graph's (the window still filling, a different
+ * key split), the graph is first rebuilt for them; *rebuilt (may be NULL) is
+ * 1 then.  Results are those of wm_rollout_step either way.
+ * The graph and its executable instance are HIP objects the library creates
+ * (host and driver memory); the ring's pool and the tensors stay the
+ * caller's.  wm_rollout_graph_destroy releases them; a graph must not
+ * outlive its ring.
+ * Errors: as wm_rollout_step; WM_E_STATE for a dead graph handle. */
+wm_status wm_rollout_graph_create(wm_kvring* ring, int32_t n_denoise, const wm_bf16* const* q,
+                                  const wm_bf16* const* k, const wm_bf16* const* v,
+                                  int32_t n_frames, const uint8_t* active, wm_bf16* q_rot_scratch,
+                                  wm_bf16* k_rot_scratch, wm_bf16* const* out, void* workspace,
+                                  size_t workspace_bytes, wm_rollout_graph** graph_out);
+wm_status wm_rollout_graph_launch(wm_rollout_graph* graph, wm_append_report* rep,
+                                  int32_t* rebuilt, void* stream);
+wm_status wm_rollout_graph_destroy(wm_rollout_graph* graph);
 
 /* Thread-local message for the last non-OK status ("" if none). */
 const char* wm_last_error(void);

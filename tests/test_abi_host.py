@@ -263,7 +263,10 @@ def test_call_errors_leave_state_unchanged():
     assert L.wm_rope3d(r._h, p, p, 4, 1, None, None, None) == 3
     assert L.wm_chunk_attn(r._h, p, p, p, 1, None, 0.0, p, None, 0, None) == 3
     arr = (ctypes.c_void_p * 1)(p)
-    assert L.wm_rollout_step(r._h, 1, arr, arr, arr, 1, None, p, p, arr, None, 0, None, None) == 3
+    assert L.wm_rollout_step(r._h, 1, arr, arr, arr, 1, None, p, p, arr, None, 0, None, None, None) == 3
+    h = ctypes.c_void_p()
+    assert L.wm_rollout_graph_create(r._h, 1, arr, arr, arr, 1, None, p, p, arr, None, 0, ctypes.byref(h)) == 3
+    assert not h.value
     assert [r.view(b) for b in range(2)] == before
     # success clears the message
     r.view(0)
@@ -325,4 +328,17 @@ def test_reset_policy_with_no_window_stores_sinks_only():
     with pytest.raises(wm.WMError) as e:
         r.append_evict(None, None, 1)
     assert e.value.name == "WM_E_CAPACITY"
+    r.close()
+
+
+def test_graph_handles_are_checked():
+    L = wm.lib()
+    used = ctypes.c_int32(7)
+    assert L.wm_rollout_graph_launch(None, None, ctypes.byref(used), None) == 3
+    assert L.wm_rollout_graph_destroy(None) == 3
+    # a ring handle is not a graph handle, and the other way round
+    r = wm.KVRing(1, 2, 2, 64, 2, 2, 1, 1, 1, meta_only=True)
+    assert L.wm_rollout_graph_launch(r._h, None, ctypes.byref(used), None) == 3
+    assert L.wm_rollout_graph_destroy(r._h) == 3
+    assert used.value == 7
     r.close()

@@ -1,0 +1,123 @@
+"""GPU: a rollout step as a HIP graph, and the append on a finalize stream.
+
+Three rings start identical and run the same chunks: one through
+wm_rollout_step on one stream (eager), one through wm_rollout_graph_launch
+(the graph's buffers are refilled with each chunk's inputs), one through
+wm_rollout_step with a separate finalize stream.  Every chunk's outputs,
+append reports and pool bytes must be identical bit for bit, through the
+window filling (where the launch shapes may change and the graph is
+rebuilt) and steady state (where only its node parameters are refreshed).  Between
+graph launches the test does unrelated eager work and synchronizes, and the
+first steady-state chunk is also checked against the fp64 oracle.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import autoregressive_video_world_amd as wm
+from oracle.rollout import Rollout
+from wm_synth import Source, Workload
+from gpu_util import assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "mha_c2": Workload(401, "graph_mha", 1, 4, 4, 128, 10, 10, 2, 1, 3, 0, 14, 2),
+    "gqa_batch2": Workload(402, "graph_gqa", 2, 8, 2, 128, 7, 9, 1, 1, 2, 0, 8, 2),
+    "d64_c3": Workload(403, "graph_d64", 1, 2, 2, 64, 5, 10, 3, 1, 4, 0, 15, 1),
+}
+
+
+def new_ring(wl):
+    """A ring over a zero-filled pool (filled before create: the RoPE tables live in the pool)."""
+    meta = wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                     wl.n_sink, wl.window, wl.chunk, meta_only=True)
+    pool = torch.zeros(meta.pool_bytes, dtype=torch.uint8, device="cuda")
+    meta.close()
+    return wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                     wl.n_sink, wl.window, wl.chunk, pool=pool)
+
+
+@pytest.mark.parametrize("name,split", [("mha_c2", False), ("gqa_batch2", False), ("gqa_batch2", True),
+                                        ("d64_c3", False)])
+def test_graph_and_finalize_stream_match_eager(name, split):
+    wl = CASES[name]
+    print("case", name, "split", split, flush=True)
+    old = os.environ.get("WM_ATTN_SPLIT")
+    if split:
+        os.environ["WM_ATTN_SPLIT"] = "3"
+    try:
+        _run(wl, split)
+    finally:
+        if old is None:
+            os.environ.pop("WM_ATTN_SPLIT", None)
+        else:
+            os.environ["WM_ATTN_SPLIT"] = old
+
+
+def _run(wl, split):
+    B, C, D = wl.batch, wl.chunk, wl.n_denoise
+    src = Source(wl)
+    eager, graphed, overl = new_ring(wl), new_ring(wl), new_ring(wl)
+    ws_bytes = eager.workspace_bytes(C)
+    if split:
+        assert ws_bytes > 0
+    wss = [torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda") if ws_bytes else None
+           for _ in range(3)]
+    shape_q = (B, C * wl.ft, wl.n_q_heads, wl.head_dim)
+    shape_k = (B, C * wl.ft, wl.n_kv_heads, wl.head_dim)
+    gq = [torch.empty(shape_q, dtype=torch.bfloat16, device="cuda") for _ in range(D)]
+    gk = [torch.empty(shape_k, dtype=torch.bfloat16, device="cuda") for _ in range(D)]
+    gv = [torch.empty(shape_k, dtype=torch.bfloat16, device="cuda") for _ in range(D)]
+    graph = graphed.rollout_graph(gq, gk, gv, C, workspace=wss[1])
+    fin_stream = torch.cuda.Stream()
+    used = []
+    junk = torch.randn(1 << 20, device="cuda")
+    checked_oracle = False
+    for ci in range(wl.n_gen // C):
+        n0 = ci * C
+        qs = [dev(src.batch_chunk([n0] * B, C, s, "q")) for s in range(D)]
+        ks = [dev(src.batch_chunk([n0] * B, C, s, "k")) for s in range(D)]
+        vs = [dev(src.batch_chunk([n0] * B, C, s, "v")) for s in range(D)]
+        out_e, rep_e = eager.rollout_step(qs, ks, vs, C, workspace=wss[0])
+        out_e = [host(o) for o in out_e]
+        for s in range(D):
+            gq[s].copy_(qs[s])
+            gk[s].copy_(ks[s])
+            gv[s].copy_(vs[s])
+        out_g, rep_g = graph.launch()
+        used.append(graph.rebuilt)
+        out_g = [host(o) for o in out_g]
+        # unrelated eager work and a synchronization between graph launches
+        junk.mul_(1.0001).add_(0.5)
+        torch.cuda.synchronize()
+        out_o, rep_o = overl.rollout_step(qs, ks, vs, C, workspace=wss[2], finalize_stream=fin_stream)
+        out_o = [host(o) for o in out_o]
+        assert rep_g == rep_e and rep_o == rep_e, ci
+        for s in range(D):
+            assert np.array_equal(out_g[s], out_e[s]), ("graph", ci, s)
+            assert np.array_equal(out_o[s], out_e[s]), ("finalize stream", ci, s)
+        torch.cuda.synchronize()
+        for r in (graphed, overl):
+            assert torch.equal(r.pool_k(), eager.pool_k()) and torch.equal(r.pool_v(), eager.pool_v()), ci
+        # the oracle, once the window is full
+        if not checked_oracle and n0 >= wl.n_sink + wl.window:
+            ro = Rollout(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                         wl.n_sink, wl.window)
+            for cj in range(ci):
+                m0 = cj * C
+                ro.commit(src.batch_chunk([m0] * B, C, D - 1, "k")[0],
+                          src.batch_chunk([m0] * B, C, D - 1, "v")[0], C)
+            _, _, ref = ro.denoise_step(src.batch_chunk([n0] * B, C, 0, "q")[0],
+                                        src.batch_chunk([n0] * B, C, 0, "k")[0],
+                                        src.batch_chunk([n0] * B, C, 0, "v")[0], C)
+            assert_close(out_e[0][0], ref, "oracle chunk %d" % ci)
+            checked_oracle = True
+    assert checked_oracle
+    assert not used[-1] and not used[-2], used  # steady state: parameters refreshed, no rebuild
+    graph.close()
+    for r in (eager, graphed, overl):
+        r.close()
