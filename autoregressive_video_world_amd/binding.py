@@ -24,7 +24,7 @@ STATUS = {0: "WM_OK", 1: "WM_E_ARG", 2: "WM_E_SHAPE", 3: "WM_E_STATE", 4: "WM_E_
 
 # Every symbol include/wm.h declares.
 EXPORTS = ["wm_kvring_pool_bytes", "wm_kvring_create", "wm_kvring_destroy", "wm_kvring_reset",
-           "wm_kvring_view", "wm_rope3d", "wm_chunk_attn", "wm_chunk_attn_layer",
+           "wm_kvring_view", "wm_rope3d", "wm_rope3d_pair", "wm_chunk_attn", "wm_chunk_attn_layer",
            "wm_chunk_attn_workspace_bytes",
            "wm_kvring_append_evict", "wm_rollout_step", "wm_rollout_graph_create",
            "wm_rollout_graph_launch", "wm_rollout_graph_destroy", "wm_last_error"]
@@ -78,6 +78,7 @@ def lib():
         L.wm_kvring_reset.argtypes = [vp, i32, i64]
         L.wm_kvring_view.argtypes = [vp, i32, P(RingView)]
         L.wm_rope3d.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp]
+        L.wm_rope3d_pair.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, vp, vp, vp]
         L.wm_chunk_attn.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.c_float, vp, vp, sz, vp]
         L.wm_chunk_attn_layer.argtypes = [vp, i32, vp, vp, vp, i32, vp, ctypes.c_float, vp, vp, sz, vp]
         L.wm_chunk_attn_workspace_bytes.argtypes = [vp, i32]
@@ -206,19 +207,35 @@ class KVRing:
     def tokens(self, n_frames, heads):
         return self.batch * n_frames * self.ft * heads * self.d
 
+    def _t_first(self, t_first):
+        if t_first is None:
+            return None, None
+        arr = (ctypes.c_int64 * self.batch)(*t_first)
+        return arr, ctypes.cast(arr, ctypes.c_void_p)
+
     def rope3d(self, x, n_frames, y=None, t_first=None, active=None, stream=None):
         heads = x.shape[-2]
         if y is None:
             y = torch.empty_like(x)
         n = self.tokens(n_frames, heads)
-        tf = None
-        if t_first is not None:
-            tf_arr = (ctypes.c_int64 * self.batch)(*t_first)
-            tf = ctypes.cast(tf_arr, ctypes.c_void_p)
+        tf_arr, tf = self._t_first(t_first)
         act_arr, act = _active(active, self.batch)
         _check(lib().wm_rope3d(self._h, _ptr(x, "x", numel=n), _ptr(y, "y", numel=n), heads, n_frames,
                                tf, act, _stream(stream)))
         return y
+
+    def rope3d_pair(self, x, x2, n_frames, y=None, y2=None, t_first=None, active=None, stream=None):
+        """rope3d of x and x2 (same frames, e.g. Q and K) in one launch."""
+        h1, h2 = x.shape[-2], x2.shape[-2]
+        y = torch.empty_like(x) if y is None else y
+        y2 = torch.empty_like(x2) if y2 is None else y2
+        n1, n2 = self.tokens(n_frames, h1), self.tokens(n_frames, h2)
+        tf_arr, tf = self._t_first(t_first)
+        act_arr, act = _active(active, self.batch)
+        _check(lib().wm_rope3d_pair(self._h, _ptr(x, "x", numel=n1), _ptr(y, "y", numel=n1), h1,
+                                    _ptr(x2, "x2", numel=n2), _ptr(y2, "y2", numel=n2), h2, n_frames,
+                                    tf, act, _stream(stream)))
+        return y, y2
 
     def workspace_bytes(self, n_frames):
         return lib().wm_chunk_attn_workspace_bytes(self._h, n_frames)

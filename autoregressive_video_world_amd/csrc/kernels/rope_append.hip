@@ -26,7 +26,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int kHeads = 4;  // heads per thread
+constexpr int kHeads = kRopeHeads;  // heads per thread
 
 __device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv d) {
   return (__umulhi(n, d.mul) + n) >> d.shift;
@@ -114,7 +114,8 @@ __device__ __forceinline__ void pair_entry(const RopeParams& p, int row, int pr,
 }
 
 // grid: x = ceil(ft / tokens per block), y = row of p.rows,
-//       z = head group (rope) or 2 * (layer * head groups + head group) + part
+//       z = head group (rope: those of x, then those of x2 when paired) or
+//           2 * (layer * head groups + head group) + part
 //       (append: part 0 rotates K, part 1 copies V -- separate waves, so the V
 //       stream runs while K waves compute; all layers of a multi-layer ring in
 //       one launch, each with its own input and pool slices).
@@ -133,36 +134,42 @@ __global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p)
   if (tok >= (uint32_t)p.ft) return;
   int hgroup = kAppend ? (int)(blockIdx.z >> 1) : (int)blockIdx.z;
   const bool v_part = kAppend && (blockIdx.z & 1);
+  // Paired rope: the second tensor (its own heads and stride, the same rows).
+  const bool second = !kAppend && hgroup >= p.hg_first;
+  const int n_heads = second ? p.n_heads2 : p.n_heads;
+  const uint16_t* const xin = second ? p.x2 : p.x;
+  const int64_t x_b_stride = second ? p.x2_b_stride : p.x_b_stride;
+  if (second) hgroup -= p.hg_first;
   int64_t x_layer = 0, pool_layer = 0;
   if constexpr (kAppend) {
-    const int n_hg = (p.n_heads + kHeads - 1) / kHeads;
+    const int n_hg = (n_heads + kHeads - 1) / kHeads;
     const int layer = hgroup / n_hg;
     hgroup -= layer * n_hg;
     x_layer = (int64_t)layer * p.x_layer_stride;
     pool_layer = (int64_t)layer * p.pool_layer_stride;
   }
   const int h0 = hgroup * kHeads;
-  const int nh = min(kHeads, p.n_heads - h0);
+  const int nh = min(kHeads, n_heads - h0);
   const int rb = p.rows[row].b;
   const int rj = p.rows[row].j;
   const uint32_t head_bytes = (uint32_t)kCpr * 16u;
 
   // A frame of the chunk holds below 2^28 elements: 32-bit byte offsets.
   // Heads past the last are clamped on load; their stores are skipped.
-  const int64_t row_base = x_layer + (int64_t)rb * p.x_b_stride + (int64_t)rj * p.ft * p.n_heads * (kCpr * 8);
-  const uint32_t src_off = ((tok * (uint32_t)p.n_heads + h0) * kCpr + c8) * 16u;
+  const int64_t row_base = x_layer + (int64_t)rb * x_b_stride + (int64_t)rj * p.ft * n_heads * (kCpr * 8);
+  const uint32_t src_off = ((tok * (uint32_t)n_heads + h0) * kCpr + c8) * 16u;
 
   // Destinations: the chunk layout (rope) or the slot's [head][token][d] block.
   char* out;
   uint32_t dst_off, dst_head;
   if constexpr (kAppend) {
     const int64_t slot_base =
-        pool_layer + ((int64_t)rb * p.ring_slots + p.rows[row].slot) * p.n_heads * p.ft * (kCpr * 8);
+        pool_layer + ((int64_t)rb * p.ring_slots + p.rows[row].slot) * n_heads * p.ft * (kCpr * 8);
     out = reinterpret_cast<char*>((v_part ? p.vdst : p.y) + slot_base);
     dst_head = (uint32_t)p.ft * head_bytes;
     dst_off = (uint32_t)h0 * dst_head + (tok * kCpr + c8) * 16u;
   } else {
-    out = reinterpret_cast<char*>(p.y + row_base);
+    out = reinterpret_cast<char*>((second ? p.y2 : p.y) + row_base);
     dst_head = head_bytes;
     dst_off = src_off;
   }
@@ -188,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p)
 #pragma unroll
   for (int k = 0; k < 4; ++k) pair_entry(p, row, (int)c8 * 4 + k, hpos, wpos, c[k], s[k]);
 
-  const char* xs = reinterpret_cast<const char*>(p.x + row_base) + src_off;
+  const char* xs = reinterpret_cast<const char*>(xin + row_base) + src_off;
   u32x4 kx[kHeads];
 #pragma unroll
   for (int g = 0; g < kHeads; ++g)
@@ -223,8 +230,9 @@ LaunchSpec rows_spec(const RopeParams& p) {
   const int lg = p.lg_cpr;
   const uint32_t tpb = kThreads >> lg;
   LaunchSpec sp;
-  sp.grid = dim3((p.ft + tpb - 1) / tpb, p.n_rows,
-                 (kAppend ? 2 * p.n_layers : 1) * ((p.n_heads + kHeads - 1) / kHeads));
+  const int hg = (p.n_heads + kHeads - 1) / kHeads;
+  const int hg2 = !kAppend && p.x2 ? (p.n_heads2 + kHeads - 1) / kHeads : 0;
+  sp.grid = dim3((p.ft + tpb - 1) / tpb, p.n_rows, kAppend ? 2 * p.n_layers * hg : hg + hg2);
   sp.block = dim3(kThreads);
   sp.func = lg == 4 ? reinterpret_cast<const void*>(&rope_rows_kernel<kAppend, 4>)
                     : reinterpret_cast<const void*>(&rope_rows_kernel<kAppend, 3>);

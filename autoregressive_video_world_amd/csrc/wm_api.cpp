@@ -53,6 +53,14 @@ bool sync_check_enabled() {
   return on;
 }
 
+// WM_FAULT_INJECT=launch|rope|attn|append (read on every call): direct
+// launches of that kind (every kind for "launch") fail as if the runtime had
+// refused them; for tests of the error path.
+bool fault_injected(const char* kind) {
+  const char* e = getenv("WM_FAULT_INJECT");
+  return e && (strcmp(e, "launch") == 0 || strcmp(e, kind) == 0);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -250,8 +258,7 @@ void fill_tables_ptrs(const wm_kvring* r, wm::RopeParams* p, int n_heads) {
   p->w_base = r->desc.frame_h * (r->bands.dh / 2);
   p->n_heads = n_heads;
   p->lg_cpr = r->desc.head_dim == 128 ? 4 : 3;
-  p->row_vecs = r->ft * n_heads * (r->desc.head_dim / 8);
-  p->div_heads = fast_div_of((uint32_t)n_heads);
+  p->hg_first = (n_heads + wm::kRopeHeads - 1) / wm::kRopeHeads;
   p->div_fw = fast_div_of((uint32_t)r->desc.frame_w);
   p->div_fh = fast_div_of((uint32_t)r->desc.frame_h);
   p->fh = r->desc.frame_h;
@@ -309,7 +316,8 @@ struct Sink {
   hipStream_t s = nullptr;
   std::vector<PLaunch>* rec = nullptr;
 
-  hipError_t put(const wm::LaunchSpec& sp, const wm::RopeParams* rp, const wm::AttnParams* ap) {
+  hipError_t put(const wm::LaunchSpec& sp, const wm::RopeParams* rp, const wm::AttnParams* ap,
+                 const char* kind) {
     if (rec) {
       rec->emplace_back();
       PLaunch& L = rec->back();
@@ -319,18 +327,21 @@ struct Sink {
       if (ap) L.ap = *ap;
       return hipSuccess;
     }
+    if (fault_injected(kind)) return hipErrorLaunchFailure;
     void* arg = ap ? (void*)ap : (void*)rp;
     void* args[] = {arg};
     return hipLaunchKernel(sp.func, sp.grid, sp.block, args, 0, s);
   }
-  hipError_t rope(const wm::RopeParams& p) { return put(wm::rope3d_spec(p), &p, nullptr); }
-  hipError_t append(const wm::RopeParams& p) { return put(wm::kv_append_spec(p), &p, nullptr); }
+  hipError_t rope(const wm::RopeParams& p) { return put(wm::rope3d_spec(p), &p, nullptr, "rope"); }
+  hipError_t append(const wm::RopeParams& p) {
+    return put(wm::kv_append_spec(p), &p, nullptr, "append");
+  }
   hipError_t attn(wm::AttnParams p, int head_dim) {
     wm::LaunchSpec sp[2];
     const int n = wm::chunk_attn_specs(p, head_dim, sp);
     if (n == 0) return hipErrorInvalidValue;
     for (int i = 0; i < n; ++i) {
-      hipError_t e = put(sp[i], nullptr, &p);
+      hipError_t e = put(sp[i], nullptr, &p, "attn");
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -339,14 +350,21 @@ struct Sink {
 
 // --- the unchecked workers (arguments validated by the callers) -----------
 
+// RoPE of x into y and, when x2 is given, of x2 into y2 in the same launch
+// (Q and K of a denoise step: same frames, so the same rows and positions).
 wm_status do_rope(const wm_kvring* r, const wm_bf16* x, wm_bf16* y, int n_heads, int n_frames,
-                  const int64_t* t_first, const uint8_t* active, Sink& k) {
+                  const int64_t* t_first, const uint8_t* active, Sink& k,
+                  const wm_bf16* x2 = nullptr, wm_bf16* y2 = nullptr, int n_heads2 = 0) {
   wm::RopeParams p;
   memset(&p, 0, sizeof p);
   fill_tables_ptrs(r, &p, n_heads);
   p.x = x;
   p.y = y;
   p.x_b_stride = (int64_t)n_frames * r->ft * n_heads * r->desc.head_dim;
+  p.x2 = x2;
+  p.y2 = y2;
+  p.n_heads2 = n_heads2;
+  p.x2_b_stride = (int64_t)n_frames * r->ft * n_heads2 * r->desc.head_dim;
   for (int b = 0; b < r->desc.batch; ++b) {
     if (!is_active(active, b)) continue;
     const int64_t t0 = t_first ? t_first[b] : next_t(r, b);
@@ -444,6 +462,8 @@ wm_status do_append(wm_kvring* r, const wm_bf16* k_raw, const wm_bf16* v, int n_
       hipError_t e = k.append(p);
       if (e != hipSuccess) return hip_fail(e, "kv_append launch");
     }
+  } else if (fault_injected("append")) {  // a metadata-only ring fails where the launch would
+    return hip_fail(hipErrorLaunchFailure, "kv_append launch");
   }
   // Commit only once every launch was accepted.
   if (commit)
@@ -644,9 +664,8 @@ wm_status do_step(wm_kvring* ring, int n_denoise, const wm_bf16* const* q, const
   wm_status st;
   const wm_kvring_desc& d = ring->desc;
   for (int i = 0; i < n_denoise; ++i) {
-    if ((st = do_rope(ring, q[i], q_rot, d.n_q_heads, n_frames, nullptr, active, sink)) != WM_OK)
-      return st;
-    if ((st = do_rope(ring, k[i], k_rot, d.n_kv_heads, n_frames, nullptr, active, sink)) != WM_OK)
+    if ((st = do_rope(ring, q[i], q_rot, d.n_q_heads, n_frames, nullptr, active, sink, k[i], k_rot,
+                      d.n_kv_heads)) != WM_OK)
       return st;
     if (i == 0 && wait_stream && (st = wait_finalize(ring, wait_stream)) != WM_OK) return st;
     if ((st = do_attn(ring, 0, q_rot, k_rot, v[i], n_frames, active, 0.f, out[i], ws, ws_bytes,
@@ -685,15 +704,34 @@ hipError_t build_graph(wm_rollout_graph* g, std::vector<PLaunch>& plan) {
   return e;
 }
 
+// Drops the graph and its instance once their last launch has finished.
+// Errors of these release calls are ignored: nothing is left to report to.
 void drop_graph(wm_rollout_graph* g) {
-  if (g->launched) hipEventSynchronize(g->ev_done);
+  if (g->launched) (void)hipEventSynchronize(g->ev_done);
   g->launched = false;
-  if (g->exec) hipGraphExecDestroy(g->exec);
-  if (g->graph) hipGraphDestroy(g->graph);
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
   g->exec = nullptr;
   g->graph = nullptr;
   g->nodes.clear();
   g->shape.clear();
+}
+
+// Arguments of wm_rope3d (for each tensor of wm_rope3d_pair).
+wm_status check_rope(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, int32_t n_heads,
+                     int32_t n_frames, const int64_t* t_first, const uint8_t* active) {
+  wm_status st;
+  if ((st = check_ring(ring)) != WM_OK) return st;
+  if ((st = check_device_ring(ring)) != WM_OK) return st;
+  if ((st = check_dev(x, "x")) != WM_OK) return st;
+  if ((st = check_dev(y, "y")) != WM_OK) return st;
+  if ((st = check_frames(ring, n_frames)) != WM_OK) return st;
+  if (n_heads < 1 || n_heads > 256) return fail(WM_E_SHAPE, "n_heads %d not in [1, 256]", n_heads);
+  if (t_first)
+    for (int b = 0; b < ring->desc.batch; ++b)
+      if (is_active(active, b) && (t_first[b] < 0 || t_first[b] > ((int64_t)1 << 52)))
+        return fail(WM_E_ARG, "t_first[%d] out of range [0, 2^52]", b);
+  return WM_OK;
 }
 
 }  // namespace
@@ -768,8 +806,8 @@ wm_status wm_kvring_destroy(wm_kvring* ring) {
     std::lock_guard<std::mutex> lk(g_mu);
     g_live.erase(ring);
   }
-  if (ring->ev_attn) hipEventDestroy(ring->ev_attn);
-  if (ring->ev_fin) hipEventDestroy(ring->ev_fin);
+  if (ring->ev_attn) (void)hipEventDestroy(ring->ev_attn);
+  if (ring->ev_fin) (void)hipEventDestroy(ring->ev_fin);
   delete ring;
   return ok();
 }
@@ -815,19 +853,23 @@ wm_status wm_rope3d(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, int32_t
                     int32_t n_frames, const int64_t* t_first, const uint8_t* active,
                     void* stream) {
   wm_status st;
-  if ((st = check_ring(ring)) != WM_OK) return st;
-  if ((st = check_device_ring(ring)) != WM_OK) return st;
-  if ((st = check_dev(x, "x")) != WM_OK) return st;
-  if ((st = check_dev(y, "y")) != WM_OK) return st;
-  if ((st = check_frames(ring, n_frames)) != WM_OK) return st;
-  if (n_heads < 1 || n_heads > 256) return fail(WM_E_SHAPE, "n_heads %d not in [1, 256]", n_heads);
-  if (t_first)
-    for (int b = 0; b < ring->desc.batch; ++b)
-      if (is_active(active, b) && (t_first[b] < 0 || t_first[b] > ((int64_t)1 << 52)))
-        return fail(WM_E_ARG, "t_first[%d] out of range [0, 2^52]", b);
+  if ((st = check_rope(ring, x, y, n_heads, n_frames, t_first, active)) != WM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Sink k{s};
   if ((st = do_rope(ring, x, y, n_heads, n_frames, t_first, active, k)) != WM_OK) return st;
+  return finish(s);
+}
+
+wm_status wm_rope3d_pair(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, int32_t n_heads,
+                         const wm_bf16* x2, wm_bf16* y2, int32_t n_heads2, int32_t n_frames,
+                         const int64_t* t_first, const uint8_t* active, void* stream) {
+  wm_status st;
+  if ((st = check_rope(ring, x, y, n_heads, n_frames, t_first, active)) != WM_OK) return st;
+  if ((st = check_rope(ring, x2, y2, n_heads2, n_frames, t_first, active)) != WM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Sink k{s};
+  if ((st = do_rope(ring, x, y, n_heads, n_frames, t_first, active, k, x2, y2, n_heads2)) != WM_OK)
+    return st;
   return finish(s);
 }
 
@@ -972,7 +1014,7 @@ wm_status wm_rollout_graph_create(wm_kvring* ring, int32_t n_denoise, const wm_b
   if (e == hipSuccess) e = build_graph(g, plan);
   if (e != hipSuccess) {
     drop_graph(g);
-    if (g->ev_done) hipEventDestroy(g->ev_done);
+    if (g->ev_done) (void)hipEventDestroy(g->ev_done);
     delete g;
     return hip_fail(e, "graph build");
   }
@@ -1037,7 +1079,7 @@ wm_status wm_rollout_graph_destroy(wm_rollout_graph* g) {
     g_graphs.erase(g);
   }
   drop_graph(g);
-  hipEventDestroy(g->ev_done);
+  (void)hipEventDestroy(g->ev_done);
   delete g;
   return ok();
 }

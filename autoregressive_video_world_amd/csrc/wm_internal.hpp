@@ -13,6 +13,7 @@ namespace wm {
 // ---------------------------------------------------------------------------
 constexpr int kRopeRows = 8;     // (rollout, frame) rows per launch
 constexpr int kMaxTPairs = 32;   // d_t / 2 upper bound
+constexpr int kRopeHeads = 4;    // heads per thread of the RoPE / append kernel
 
 struct RopeRow {
   int32_t b;      // rollout index
@@ -36,13 +37,17 @@ struct RopeParams {
   uint16_t* vdst;         // append only: V half of the pool
   const double2* hw;      // (cos, sin) table: [frame_h][dh2] of the h band, then
                           // [frame_w][dw2] of the w band from entry w_base
+  const uint16_t* x2;     // rope, paired: a second chunk tensor (K with Q), same rows
+  uint16_t* y2;           // rope, paired: its output
   int64_t x_b_stride;     // elements per rollout in x / y (rope) or x / vsrc (append)
+  int64_t x2_b_stride;    // elements per rollout in x2 / y2
   int32_t n_heads;        // heads of x
+  int32_t n_heads2;       // heads of x2
+  int32_t hg_first;       // rope: head groups of x; grid z beyond them covers x2
   int32_t d;              // head dim
   int32_t lg_cpr;         // log2(d / 8): 16-byte vectors per (token, head)
   int32_t ft;             // tokens per frame
   int32_t fw;             // frame width
-  int32_t row_vecs;       // 16-byte vectors per (rollout, frame) row = ft * n_heads * d / 8
   int32_t dt2, dh2, dw2;  // pairs per band
   int32_t ring_slots;     // S + W (append)
   int32_t w_base;         // first entry of the w band in hw
@@ -50,7 +55,6 @@ struct RopeParams {
   int32_t n_layers;       // append: layers written by one launch (rope: 1)
   int64_t x_layer_stride;     // append: elements between layers of x / vsrc
   int64_t pool_layer_stride;  // append: elements between layers of y / vdst
-  FastDiv div_heads;      // division by n_heads
   FastDiv div_fw;         // division by frame width
   FastDiv div_fh;         // division by frame height (token -> row within its view)
   int32_t fh;             // frame height (rows of one view)

@@ -35,8 +35,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", type=int, default=2, help="workload id (1-5), default 2")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -45,6 +45,9 @@ def parse():
                     help="layers of the multi-layer append measurement (0 = skip)")
     ap.add_argument("--views-workload", type=int, default=6,
                     help="multi-view workload whose steady-state attention is also timed (0 = skip)")
+    ap.add_argument("--modes-workload", type=int, default=1,
+                    help="second workload whose rollout step is timed eager / finalize stream / graph "
+                         "(0: none)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain elementwise copy of this many MiB first (untimed), as the "
                          "known-size reference for HBM byte counters")
@@ -122,6 +125,49 @@ def cpu_baseline(wl, n_heads):
                       % (wl.name, wl.nq, wl.steady_keys(), len(heads), wl.n_q_heads, dt)}
 
 
+def rollout_modes(torch, wm, wl, randn, dev, steps, warmup, ring=None):
+    """ms per steady-state rollout step, launched three ways: every launch
+    from the host on one stream; the append on a second (finalize) stream;
+    the step's launches replayed from a HIP graph."""
+    own = ring is None
+    if own:
+        ring = wm.KVRing(1, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                         wl.n_sink, wl.window, wl.chunk, device=dev, n_views=wl.n_views)
+        for _ in range(wl.n_sink + wl.window):
+            ring.append_evict(randn(1, wl.ft, wl.n_kv_heads, wl.head_dim),
+                              randn(1, wl.ft, wl.n_kv_heads, wl.head_dim), 1)
+    C, D, ft = wl.chunk, wl.n_denoise, wl.ft
+    qs = [randn(1, C * ft, wl.n_q_heads, wl.head_dim) for _ in range(D)]
+    ks = [randn(1, C * ft, wl.n_kv_heads, wl.head_dim) for _ in range(D)]
+    vs = [randn(1, C * ft, wl.n_kv_heads, wl.head_dim) for _ in range(D)]
+    outs = [torch.empty_like(q) for q in qs]
+    q_rot, k_rot = torch.empty_like(qs[0]), torch.empty_like(ks[0])
+    ws_bytes = ring.workspace_bytes(C)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    fin = torch.cuda.Stream()
+    graph = ring.rollout_graph(qs, ks, vs, C, outs=outs, q_rot_scratch=q_rot, k_rot_scratch=k_rot,
+                               workspace=ws)
+    kw = dict(outs=outs, q_rot_scratch=q_rot, k_rot_scratch=k_rot, workspace=ws)
+    modes = {"eager": lambda: ring.rollout_step(qs, ks, vs, C, **kw),
+             "finalize_stream": lambda: ring.rollout_step(qs, ks, vs, C, finalize_stream=fin, **kw),
+             "graph": graph.launch}
+    res = {}
+    for name, fn in modes.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        res[name + "_ms_per_step"] = round((time.perf_counter() - t0) / steps * 1e3, 4)
+    res["graph_rebuilt_in_steady_state"] = bool(graph.rebuilt)
+    graph.close()
+    if own:
+        ring.close()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -196,10 +242,20 @@ def main():
     # duration of a launch in a busy stream.  Short launches (RoPE, append)
     # are queued behind one attention launch, so that, as in a rollout, the
     # host-side cost of each call (measured separately) overlaps GPU work
-    # instead of leaving the GPU idle between launches.
+    # instead of leaving the GPU idle between launches.  Before each loop the
+    # GPU runs attention launches for about 100 ms: after an idle gap of even
+    # 50 ms the clock takes tens of milliseconds to return to its sustained
+    # level under load, which would otherwise inflate the first launches.
+    def heat(seconds=0.1):
+        t = time.perf_counter()
+        while time.perf_counter() - t < seconds:
+            attn()
+            torch.cuda.synchronize()
+
     def timed(fn, reps, behind=None):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
+        heat()
         fn()
         torch.cuda.synchronize()
         if behind is not None:
@@ -217,7 +273,9 @@ def main():
     ring.rope3d(ks[0], C, y=k_rot)
     attn = lambda: ring.chunk_attn(q_rot, k_rot, vs[0], C, out=outs[0], workspace=ws)
     attn_mean, _ = timed(attn, args.kernel_reps)
-    rope_q_mean, rope_host_us = timed(lambda: ring.rope3d(qs[0], C, y=q_rot), args.kernel_reps, attn)
+    rope_mean, rope_host_us = timed(lambda: ring.rope3d_pair(qs[0], ks[0], C, y=q_rot, y2=k_rot),
+                                    args.kernel_reps, attn)
+    rope_q_mean, _ = timed(lambda: ring.rope3d(qs[0], C, y=q_rot), args.kernel_reps, attn)
     rope_k_mean, _ = timed(lambda: ring.rope3d(ks[0], C, y=k_rot), args.kernel_reps, attn)
     app_mean, app_host_us = timed(lambda: ring.append_evict(ks[-1], vs[-1], C), args.kernel_reps, attn)
     # The same append with its inputs rotated over more than twice the
@@ -305,13 +363,26 @@ def main():
         vring.close()
         del vq, vk, vv, vo, vws
 
+    # The same step launched from the finalize stream and from a HIP graph,
+    # here and on a workload small enough that launch costs show.
+    modes = {"workload": wl.name, **rollout_modes(torch, wm, wl, randn, dev, args.steps,
+                                                  args.warmup, ring)}
+    modes_small = None
+    if args.modes_workload and args.modes_workload != args.workload:
+        mw = WORKLOADS[args.modes_workload]
+        modes_small = {"workload": "%s: %d q/%d kv heads, d %d, %dx%d tokens/frame, chunk %d, "
+                                   "%d sink + %d window frames, %d denoise steps"
+                                   % (mw.name, mw.n_q_heads, mw.n_kv_heads, mw.head_dim, mw.frame_h,
+                                      mw.frame_w, mw.chunk, mw.n_sink, mw.window, mw.n_denoise),
+                       **rollout_modes(torch, wm, mw, randn, dev, max(args.steps, 200), args.warmup)}
+
     attn_tflops = wl.attn_flops() / (attn_mean * 1e-3) / 1e12
     app_bytes = wl.append_bytes()
     app_gbs = app_bytes / (app_mean * 1e-3) / 1e9
     app_cold_gbs = app_bytes / (app_cold_mean * 1e-3) / 1e9
     copy_cold_gbs = app_bytes / (copy_cold_mean * 1e-3) / 1e9
     rope_bytes = 2 * wl.nq * wl.head_dim * 2 * (wl.n_q_heads + wl.n_kv_heads)
-    rope_gbs = rope_bytes / ((rope_q_mean + rope_k_mean) * 1e-3) / 1e9
+    rope_gbs = rope_bytes / (rope_mean * 1e-3) / 1e9
     prof_traffic = profiled_traffic(wl.name)
 
     result = {
@@ -333,7 +404,7 @@ def main():
                                   "%d views of " % wl.n_views if wl.n_views > 1 else "", wl.frame_h,
                                   wl.frame_w, C, wl.nq, wl.n_sink, wl.window, wl.steady_keys(), D),
                    "batch": 1, "n_q": wl.nq, "n_k": wl.steady_keys(), "denoise_steps": D},
-        "denoise_steps_per_s_per_chunk": round(1e3 / (attn_mean + rope_q_mean + rope_k_mean), 2),
+        "denoise_steps_per_s_per_chunk": round(1e3 / (attn_mean + rope_mean), 2),
         "chunks_per_s": round(1e3 / ms_per_step, 3),
         "attn_pct_mfma_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "kernel": "chunk_attn_kernel<128>",
@@ -348,12 +419,13 @@ def main():
                    "achieved_inputs_from_hbm": round(app_cold_gbs, 1),
                    "frac_inputs_from_hbm": round(app_cold_gbs / PEAK_HBM_GBS, 4),
                    "copy_same_bytes_from_hbm": round(copy_cold_gbs, 1)},
+        "rollout_modes": [modes] + ([modes_small] if modes_small else []),
         "append_layers": layers,
         "views": views,
         "rope": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
-                 "launch_ms_mean_q": round(rope_q_mean, 5), "launch_ms_mean_k": round(rope_k_mean, 5),
-                 "host_us_per_call": round(rope_host_us, 1)},
+                 "launch_ms_mean": round(rope_mean, 5), "host_us_per_call": round(rope_host_us, 1),
+                 "q_and_k_as_two_launches_gbs": round(rope_bytes / ((rope_q_mean + rope_k_mean) * 1e-3) / 1e9, 1)},
         "cpu_baseline": None,
     }
     ring.close()

@@ -41,11 +41,19 @@
  *  - The library allocates no device memory.  The caller owns the pool, all
  *    tensors, workspaces, host report/view structs and streams.
  *  - Errors: every argument is validated before anything is enqueued.  A
- *    non-zero status means nothing was enqueued and the ring is unchanged;
- *    wm_last_error() then returns a message (thread-local).  Device faults are
- *    asynchronous and surface at the caller's next synchronization; with the
- *    environment variable WM_SYNC_CHECK=1 every call synchronizes its stream
- *    and reports such errors as WM_E_HIP.
+ *    non-zero status other than WM_E_HIP means nothing was enqueued and the
+ *    ring is unchanged; wm_last_error() then returns a message
+ *    (thread-local).  WM_E_HIP from a launch the runtime refused: launches
+ *    of the same call before it may have been enqueued, the ring's
+ *    bookkeeping (frames, slots, positions) is unchanged, but slots this call
+ *    would have written may hold part of the new data -- wm_kvring_reset of
+ *    the affected rollouts recovers.  Device faults are asynchronous and
+ *    surface at the caller's next synchronization; with the environment
+ *    variable WM_SYNC_CHECK=1 every call synchronizes its stream and reports
+ *    such errors as WM_E_HIP.  WM_FAULT_INJECT=launch|rope|attn|append (read
+ *    on every call, for tests of this path) makes every direct launch of that
+ *    kind ("launch": any) fail that way; on a metadata-only ring "append"
+ *    fails wm_kvring_append_evict at the point of its launch.
  *  - A ring is not thread-safe; calls on one ring must be ordered on one
  *    stream (or by the caller's events).
  */
@@ -192,6 +200,16 @@ wm_status wm_kvring_view(const wm_kvring* ring, int32_t b, wm_ring_view* out);
  * WM_E_STATE (metadata-only ring), WM_E_HIP. */
 wm_status wm_rope3d(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, int32_t n_heads,
                     int32_t n_frames, const int64_t* t_first, const uint8_t* active, void* stream);
+
+/* wm_rope3d of two tensors of the same chunk frames (the Q and K of one
+ * denoise step) in one launch: x (n_heads) into y and x2 (n_heads2) into y2,
+ * each with its own [B][n_frames*Ft][heads][d] layout and the same positions.
+ * Results are bit-identical to two wm_rope3d calls.  y may equal x and y2
+ * may equal x2; the pair (x, y) must not overlap (x2, y2).
+ * Errors: as wm_rope3d, for either tensor. */
+wm_status wm_rope3d_pair(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, int32_t n_heads,
+                         const wm_bf16* x2, wm_bf16* y2, int32_t n_heads2, int32_t n_frames,
+                         const int64_t* t_first, const uint8_t* active, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Chunk attention (one denoise step; FlashDreams generate()).

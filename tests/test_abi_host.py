@@ -261,6 +261,7 @@ def test_call_errors_leave_state_unchanged():
     # device calls on a metadata-only ring
     p = ctypes.c_void_p(0x1000)
     assert L.wm_rope3d(r._h, p, p, 4, 1, None, None, None) == 3
+    assert L.wm_rope3d_pair(r._h, p, p, 4, p, p, 2, 1, None, None, None) == 3
     assert L.wm_chunk_attn(r._h, p, p, p, 1, None, 0.0, p, None, 0, None) == 3
     arr = (ctypes.c_void_p * 1)(p)
     assert L.wm_rollout_step(r._h, 1, arr, arr, arr, 1, None, p, p, arr, None, 0, None, None, None) == 3
@@ -341,4 +342,29 @@ def test_graph_handles_are_checked():
     assert L.wm_rollout_graph_launch(r._h, None, ctypes.byref(used), None) == 3
     assert L.wm_rollout_graph_destroy(r._h) == 3
     assert used.value == 7
+    r.close()
+
+
+def test_refused_append_launch_keeps_bookkeeping(monkeypatch):
+    """WM_FAULT_INJECT=append on a metadata-only ring: the append fails with
+    WM_E_HIP where its launch would be, the bookkeeping is unchanged, other
+    kinds do not touch it, and a reset starts a clean sequence."""
+    r = wm.KVRing(2, 4, 2, 128, 4, 5, 1, 3, 2, meta_only=True)
+    r.append_evict(None, None, 2)
+    r.append_evict(None, None, 2)
+    before = [r.view(b) for b in range(2)]
+    monkeypatch.setenv("WM_FAULT_INJECT", "append")
+    with pytest.raises(wm.WMError) as e:
+        r.append_evict(None, None, 2)
+    assert e.value.name == "WM_E_HIP"
+    assert [r.view(b) for b in range(2)] == before
+    monkeypatch.setenv("WM_FAULT_INJECT", "attn")
+    reps = r.append_evict(None, None, 1, active=[1, 0])
+    assert reps[0]["written"] == [(4, 1, 4)] and reps[0]["evicted"] == [1]   # (frame, slot, t)
+    assert r.view(1) == before[1]
+    monkeypatch.delenv("WM_FAULT_INJECT")
+    r.reset(1, 50)
+    r.append_evict(None, None, 2, active=[0, 1])
+    v = r.view(1)
+    assert [(f, t) for f, _, t in v["retained"]] == [(0, 50), (1, 51)] and v["t0"] == 50
     r.close()

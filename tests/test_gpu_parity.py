@@ -335,6 +335,38 @@ def test_rope_explicit_t_first_and_inactive_rows_untouched():
     ring.close()
 
 
+@pytest.mark.parametrize("d,hq,hkv,views", [(128, 6, 3, 1), (64, 9, 3, 2)])
+def test_rope_pair_equals_two_single_launches(d, hq, hkv, views):
+    """wm_rope3d_pair (Q and K in one launch; head counts that leave a partial
+    head group on either side) against the oracle and against two wm_rope3d
+    calls, with explicit t_first, an inactive rollout and full-range bits."""
+    B, fh, fw, n = 3, 3, 5, 2
+    ft = views * fh * fw
+    q = full_range_bits(150 + d, (B, n * ft, hq, d))
+    k = full_range_bits(151 + d, (B, n * ft, hkv, d))
+    wl = W(150, batch=B, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, frame_h=fh, frame_w=fw, chunk=n,
+           n_views=views)
+    ring, _ = make_ring(wl)
+    t_first, active = [17, 4, 70001], [1, 0, 1]
+    yq = torch.full(q.shape, 3.0, dtype=torch.bfloat16, device="cuda")
+    yk = torch.full(k.shape, 3.0, dtype=torch.bfloat16, device="cuda")
+    ring.rope3d_pair(dev(q), dev(k), n, y=yq, y2=yk, t_first=t_first, active=active)
+    gq, gk = host(yq), host(yk)
+    sq = host(ring.rope3d(dev(q), n, t_first=t_first, active=active))
+    sk = host(ring.rope3d(dev(k), n, t_first=t_first, active=active))
+    three = host(torch.full((1,), 3.0, dtype=torch.bfloat16))[0]
+    for b in range(B):
+        if not active[b]:
+            assert np.all(gq[b] == three) and np.all(gk[b] == three), b
+            continue
+        t, h, w = orope.token_positions(n, fh, fw, t_first[b], n_views=views)
+        with np.errstate(invalid="ignore", over="ignore"):  # inf and NaN inputs
+            assert np.array_equal(gq[b], orope.rotate(q[b], t, h, w)), ("q", b)
+            assert np.array_equal(gk[b], orope.rotate(k[b], t, h, w)), ("k", b)
+        assert np.array_equal(gq[b], sq[b]) and np.array_equal(gk[b], sk[b]), b
+    ring.close()
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads, steady state, sampled outputs
 # ---------------------------------------------------------------------------

@@ -90,3 +90,63 @@ def test_reset_window_cfg_pair(chunk):
             oracles[b].reset(0)
         assert ring.view(0)["retained"] == []
     ring.close()
+
+
+@pytest.mark.parametrize("kind", ["launch", "attn", "append"])
+def test_refused_launch_mid_step_then_reset(kind, monkeypatch):
+    """A launch the runtime refuses (forced with WM_FAULT_INJECT) inside a
+    rollout step whose append would evict: the step fails with WM_E_HIP, the
+    bookkeeping and the pool bytes are unchanged (the append is the only
+    launch that writes the pool), and after wm_kvring_reset the rollouts
+    continue exactly as fresh oracle sequences."""
+    wl = Workload(311, "fault", 2, 4, 2, 64, 5, 7, 2, 1, 3, 0, 0, 2)
+    src = Source(wl)
+    B, S, W, C, D = 2, wl.n_sink, wl.window, wl.chunk, wl.n_denoise
+    ring = wm.KVRing(B, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w, S, W, C)
+    oracles = [Rollout(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w, S, W)
+               for _ in range(B)]
+    seq = 0
+    while seq < S + W:   # fill sinks and window
+        n = min(C, S + W - seq)
+        ring.append_evict(dev(src.batch_chunk([seq] * B, n, -1, "k")),
+                          dev(src.batch_chunk([seq] * B, n, -1, "v")), n)
+        seq += n
+
+    def step_inputs(n0):
+        return [[dev(src.batch_chunk([n0] * B, C, s, x)) for s in range(D)] for x in "qkv"]
+
+    views = [ring.view(b) for b in range(B)]
+    torch.cuda.synchronize()
+    pool = ring.pool.clone()
+    qs, ks, vs = step_inputs(seq)
+    monkeypatch.setenv("WM_FAULT_INJECT", kind)
+    with pytest.raises(wm.WMError) as e:
+        ring.rollout_step(qs, ks, vs, C)
+    monkeypatch.delenv("WM_FAULT_INJECT")
+    assert e.value.name == "WM_E_HIP"
+    assert [ring.view(b) for b in range(B)] == views
+    torch.cuda.synchronize()
+    assert torch.equal(pool, ring.pool)
+
+    # recovery: new sequences at new origins, one conditioning frame, two steps
+    for b in range(B):
+        ring.reset(b, 1000 + 7 * b)
+        oracles[b].reset(1000 + 7 * b)
+    k_np, v_np = src.batch_chunk([seq] * B, 1, -1, "k"), src.batch_chunk([seq] * B, 1, -1, "v")
+    ring.append_evict(dev(k_np), dev(v_np), 1)
+    for b in range(B):
+        oracles[b].commit(k_np[b], v_np[b], 1)
+    seq += 1
+    for _ in range(2):
+        qs, ks, vs = step_inputs(seq)
+        outs, reps = ring.rollout_step(qs, ks, vs, C)
+        for s in range(D):
+            got = host(outs[s])
+            for b in range(B):
+                _, _, ref = oracles[b].denoise_step(host(qs[s])[b], host(ks[s])[b], host(vs[s])[b], C)
+                assert_close(got[b], ref, "%s: recovered step at frame %d, b %d, s %d" % (kind, seq, b, s))
+        for b in range(B):
+            written, evicted = oracles[b].commit(host(ks[-1])[b], host(vs[-1])[b], C)
+            assert reps[b] == {"written": written, "evicted": evicted}
+        seq += C
+    ring.close()
