@@ -240,9 +240,10 @@ def main():
     # ---- per-kernel timing with HIP events on the launch stream ------------
     # `reps` launches back to back between one pair of events: the mean
     # duration of a launch in a busy stream.  Short launches (RoPE, append)
-    # are queued behind one attention launch, so that, as in a rollout, the
-    # host-side cost of each call (measured separately) overlaps GPU work
-    # instead of leaving the GPU idle between launches.  Before each loop the
+    # are queued behind a ~1 ms spin kernel that touches no memory, so that,
+    # as in a rollout, the host-side cost of each call (measured separately)
+    # overlaps GPU work instead of leaving the GPU idle between launches,
+    # while the caches hold what the untimed call left.  Before each loop the
     # GPU runs attention launches for about 100 ms: after an idle gap of even
     # 50 ms the clock takes tens of milliseconds to return to its sustained
     # level under load, which would otherwise inflate the first launches.
@@ -272,12 +273,27 @@ def main():
     ring.rope3d(qs[0], C, y=q_rot)
     ring.rope3d(ks[0], C, y=k_rot)
     attn = lambda: ring.chunk_attn(q_rot, k_rot, vs[0], C, out=outs[0], workspace=ws)
+    busy = lambda: torch.cuda._sleep(2_500_000)
     attn_mean, _ = timed(attn, args.kernel_reps)
     rope_mean, rope_host_us = timed(lambda: ring.rope3d_pair(qs[0], ks[0], C, y=q_rot, y2=k_rot),
-                                    args.kernel_reps, attn)
-    rope_q_mean, _ = timed(lambda: ring.rope3d(qs[0], C, y=q_rot), args.kernel_reps, attn)
-    rope_k_mean, _ = timed(lambda: ring.rope3d(ks[0], C, y=k_rot), args.kernel_reps, attn)
-    app_mean, app_host_us = timed(lambda: ring.append_evict(ks[-1], vs[-1], C), args.kernel_reps, attn)
+                                    args.kernel_reps, busy)
+    rope_q_mean, _ = timed(lambda: ring.rope3d(qs[0], C, y=q_rot), args.kernel_reps, busy)
+    rope_k_mean, _ = timed(lambda: ring.rope3d(ks[0], C, y=k_rot), args.kernel_reps, busy)
+    # The paired RoPE with its inputs rotated over more than twice the 256 MB
+    # last-level cache (MALL), so that every read comes from HBM.
+    rope_in = (qs[0].numel() + ks[0].numel()) * 2
+    n_rc = max(2, -(-(512 << 20) // rope_in))
+    rcold = [(randn(*qs[0].shape), randn(*ks[0].shape)) for _ in range(n_rc)]
+    rc_i = [0]
+
+    def rope_cold():
+        qc, kc = rcold[rc_i[0] % n_rc]
+        rc_i[0] += 1
+        ring.rope3d_pair(qc, kc, C, y=q_rot, y2=k_rot)
+
+    rope_cold_mean, _ = timed(rope_cold, max(args.kernel_reps, 2 * n_rc), busy)
+    del rcold
+    app_mean, app_host_us = timed(lambda: ring.append_evict(ks[-1], vs[-1], C), args.kernel_reps, busy)
     # The same append with its inputs rotated over more than twice the
     # 256 MB last-level cache (MALL), so every read comes from HBM.  In a
     # rollout the committed K and V were produced just before the commit, so
@@ -291,7 +307,7 @@ def main():
         cold_i[0] += 1
         ring.append_evict(kc, vc, C)
 
-    app_cold_mean, _ = timed(app_cold, max(args.kernel_reps, 2 * n_cold), attn)
+    app_cold_mean, _ = timed(app_cold, max(args.kernel_reps, 2 * n_cold), busy)
     del cold
     # Reference: a plain elementwise copy (torch.neg) of the same bytes, its
     # inputs rotated the same way -- what HBM delivers to a transfer this short.
@@ -304,7 +320,7 @@ def main():
         copy_i[0] += 1
         torch.neg(copy_src[a], out=copy_dst[a])
 
-    copy_cold_mean, _ = timed(copy_cold, max(args.kernel_reps, 2 * n_cold), attn)
+    copy_cold_mean, _ = timed(copy_cold, max(args.kernel_reps, 2 * n_cold), busy)
     del copy_src, copy_dst
 
     # A whole model's commit: the same workload's ring with `--layers` layers,
@@ -318,14 +334,14 @@ def main():
                           wl.n_sink, wl.window, wl.chunk, device=dev, n_layers=Ln, n_views=wl.n_views)
         lk = randn(Ln, *ks[-1].shape)
         lv = randn(Ln, *vs[-1].shape)
-        lay_mean, _ = timed(lambda: mring.append_evict(lk, lv, C), max(4, args.kernel_reps // 4), attn)
+        lay_mean, _ = timed(lambda: mring.append_evict(lk, lv, C), max(4, args.kernel_reps // 4), busy)
         per_layer = lambda: [ring.append_evict(lk[i], lv[i], C) for i in range(Ln)]
-        per_mean, _ = timed(per_layer, max(2, args.kernel_reps // 10), attn)
+        per_mean, _ = timed(per_layer, max(2, args.kernel_reps // 10), busy)
         lay_bytes = Ln * wl.append_bytes()
         del lk, lv
         csrc = randn(lay_bytes // 4)
         cdst = torch.empty_like(csrc)
-        copy_mean, _ = timed(lambda: torch.neg(csrc, out=cdst), max(4, args.kernel_reps // 4), attn)
+        copy_mean, _ = timed(lambda: torch.neg(csrc, out=cdst), max(4, args.kernel_reps // 4), busy)
         del csrc, cdst
         layers = {"bound": "hbm", "layers": Ln, "bytes_per_launch": lay_bytes,
                   "achieved": round(lay_bytes / (lay_mean * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
@@ -425,6 +441,8 @@ def main():
         "rope": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
                  "launch_ms_mean": round(rope_mean, 5), "host_us_per_call": round(rope_host_us, 1),
+                 "achieved_inputs_from_hbm": round(rope_bytes / (rope_cold_mean * 1e-3) / 1e9, 1),
+                 "frac_inputs_from_hbm": round(rope_bytes / (rope_cold_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                  "q_and_k_as_two_launches_gbs": round(rope_bytes / ((rope_q_mean + rope_k_mean) * 1e-3) / 1e9, 1)},
         "cpu_baseline": None,
     }
