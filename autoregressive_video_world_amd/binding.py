@@ -297,6 +297,12 @@ class KVRing:
                                            k_rot_scratch, workspace)
         fs = None if finalize_stream is None else _stream(finalize_stream)
         _check(lib().wm_rollout_step(self._h, *args, self._reps_ptr, _stream(stream), fs))
+        if finalize_stream is not None:
+            # the append reads the last step's K and V there after this call
+            # returns: the caching allocator must not hand their memory out
+            # before that stream has passed it
+            ks[-1].record_stream(finalize_stream)
+            vs[-1].record_stream(finalize_stream)
         return outs, [_report_dict(r) for r in self._reps]
 
     def rollout_graph(self, qs, ks, vs, n_frames, outs=None, active=None, q_rot_scratch=None,

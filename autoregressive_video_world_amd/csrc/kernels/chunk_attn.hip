@@ -221,7 +221,9 @@ __global__ __launch_bounds__(512 / NQB, 1) void chunk_attn_kernel(const AttnPara
   const int col0 = __builtin_amdgcn_readfirstlane(wave) * C::COLS_PER_WAVE;
   const uint16_t* const ring_k = p.pk + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD + col0 * 8;
   const uint16_t* const ring_v = p.pv + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD + col0 * 8;
-  const uint32_t slot_stride = (uint32_t)p.hkv * ft * HD;  // elements; < 2^31 per rollout
+  // Offsets within one rollout's ring and chunk tensor stay below 2^31
+  // elements (the descriptor check at ring creation enforces it).
+  const uint32_t slot_stride = (uint32_t)p.hkv * ft * HD;
   const uint16_t* const chunk_k = p.kc + ((int64_t)b * p.nq * p.hkv + g) * HD + col0 * 8;
   const uint16_t* const chunk_v = p.vc + ((int64_t)b * p.nq * p.hkv + g) * HD + col0 * 8;
   const uint32_t chunk_stride = (uint32_t)p.hkv * HD;

@@ -154,7 +154,8 @@ __global__ __launch_bounds__(kThreads) void rope_rows_kernel(const RopeParams p)
   const int rj = p.rows[row].j;
   const uint32_t head_bytes = (uint32_t)kCpr * 16u;
 
-  // A frame of the chunk holds below 2^28 elements: 32-bit byte offsets.
+  // A rollout's chunk tensor holds below 2^31 elements (checked at ring
+  // creation), so byte offsets within a frame fit 32 bits.
   // Heads past the last are clamped on load; their stores are skipped.
   const int64_t row_base = x_layer + (int64_t)rb * x_b_stride + (int64_t)rj * p.ft * n_heads * (kCpr * 8);
   const uint32_t src_off = ((tok * (uint32_t)n_heads + h0) * kCpr + c8) * 16u;

@@ -43,6 +43,7 @@ wm_status ok() {
 
 std::mutex g_mu;
 std::set<const void*> g_live;    // live ring handles
+uint64_t g_serial = 0;           // rings created so far (a ring's serial number)
 std::set<const void*> g_graphs;  // live rollout-graph handles
 
 bool sync_check_enabled() {
@@ -142,8 +143,12 @@ wm_status check_desc(const wm_kvring_desc* d, Bands* bands) {
   const int64_t nq = (int64_t)d->max_chunk * ft_of(*d);
   if ((int64_t)(d->n_sink + d->window + d->max_chunk) * ft_of(*d) >= ((int64_t)1 << 24))
     return fail(WM_E_SHAPE, "visible keys (S+W+C)*Ft must stay below 2^24");
-  if (nq * d->n_q_heads * d->head_dim > (int64_t)1 << 31)
-    return fail(WM_E_SHAPE, "chunk tensor above 2^31 elements per rollout");
+  // The kernels form offsets within one rollout's chunk tensor and within
+  // one rollout's K (or V) half of a layer in 32 bits.
+  if (nq * d->n_q_heads * d->head_dim >= (int64_t)1 << 31)
+    return fail(WM_E_SHAPE, "chunk tensor of 2^31 elements or more per rollout");
+  if ((int64_t)(d->n_sink + d->window) * d->n_kv_heads * ft_of(*d) * d->head_dim >= (int64_t)1 << 31)
+    return fail(WM_E_SHAPE, "ring of 2^31 elements or more per rollout in the K (or V) half");
   return WM_OK;
 }
 
@@ -191,10 +196,12 @@ struct wm_kvring {
   // for ev_fin first (RoPE, which does not, overlaps it).
   hipEvent_t ev_attn = nullptr, ev_fin = nullptr;
   bool fin_recorded = false;
+  uint64_t serial = 0;  // distinguishes a ring from a later one at the same address
 };
 
 struct wm_rollout_graph {
   wm_kvring* ring;
+  uint64_t ring_serial;
   int D, n_frames;
   bool has_active;
   std::vector<uint8_t> active;
@@ -727,6 +734,8 @@ wm_status check_rope(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, int32_
   if ((st = check_dev(y, "y")) != WM_OK) return st;
   if ((st = check_frames(ring, n_frames)) != WM_OK) return st;
   if (n_heads < 1 || n_heads > 256) return fail(WM_E_SHAPE, "n_heads %d not in [1, 256]", n_heads);
+  if ((int64_t)n_frames * ring->ft * n_heads * ring->desc.head_dim >= (int64_t)1 << 31)
+    return fail(WM_E_SHAPE, "tensor of 2^31 elements or more per rollout");  // 32-bit offsets
   if (t_first)
     for (int b = 0; b < ring->desc.batch; ++b)
       if (is_active(active, b) && (t_first[b] < 0 || t_first[b] > ((int64_t)1 << 52)))
@@ -793,6 +802,7 @@ wm_status wm_kvring_create(const wm_kvring_desc* desc, void* dev_pool, size_t po
   }
   {
     std::lock_guard<std::mutex> lk(g_mu);
+    r->serial = ++g_serial;
     g_live.insert(r);
   }
   *out = r;
@@ -992,6 +1002,7 @@ wm_status wm_rollout_graph_create(wm_kvring* ring, int32_t n_denoise, const wm_b
     return st;
   wm_rollout_graph* g = new wm_rollout_graph();
   g->ring = ring;
+  g->ring_serial = ring->serial;
   g->D = n_denoise;
   g->n_frames = n_frames;
   g->has_active = active != nullptr;
@@ -1035,6 +1046,7 @@ wm_status wm_rollout_graph_launch(wm_rollout_graph* g, wm_append_report* rep, in
   wm_status st;
   wm_kvring* ring = g->ring;
   if ((st = check_ring(ring)) != WM_OK) return st;
+  if (ring->serial != g->ring_serial) return fail(WM_E_STATE, "the graph's ring was destroyed");
   const uint8_t* active = g->has_active ? g->active.data() : nullptr;
   if ((st = check_room(ring, g->n_frames, active)) != WM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);

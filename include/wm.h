@@ -166,7 +166,9 @@ size_t wm_kvring_pool_bytes(const wm_kvring_desc* desc);
  * update the bookkeeping and reports only (no device access), and
  * wm_rope3d / wm_chunk_attn / wm_rollout_step return WM_E_STATE.
  * Errors: WM_E_ARG (NULL desc/out, misaligned pool), WM_E_SHAPE (invalid
- * descriptor), WM_E_CAPACITY (pool too small), WM_E_HIP. */
+ * descriptor, including a rollout's chunk tensor max_chunk*Ft*Hq*d or its
+ * K half (S+W)*Hkv*Ft*d reaching 2^31 elements, or (S+W+C)*Ft reaching 2^24
+ * keys), WM_E_CAPACITY (pool too small), WM_E_HIP. */
 wm_status wm_kvring_create(const wm_kvring_desc* desc, void* dev_pool, size_t pool_bytes,
                            wm_kvring** out);
 
@@ -196,8 +198,9 @@ wm_status wm_kvring_view(const wm_kvring* ring, int32_t b, wm_ring_view* out);
  * y0 = x0*c - x1*s, y1 = x0*s + x1*c in fp64 (the products are exact), then
  * rounded to bf16 round-to-nearest-even.  Only active rollouts (active[b] !=
  * 0; NULL = all) are read or written.
- * Errors: WM_E_ARG, WM_E_SHAPE (n_frames not in [1, max_chunk], n_heads < 1),
- * WM_E_STATE (metadata-only ring), WM_E_HIP. */
+ * Errors: WM_E_ARG, WM_E_SHAPE (n_frames not in [1, max_chunk], n_heads not
+ * in [1, 256], n_frames*Ft*n_heads*d of 2^31 or more), WM_E_STATE
+ * (metadata-only ring), WM_E_HIP. */
 wm_status wm_rope3d(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, int32_t n_heads,
                     int32_t n_frames, const int64_t* t_first, const uint8_t* active, void* stream);
 
@@ -299,7 +302,12 @@ wm_status wm_kvring_append_evict(wm_kvring* ring, const wm_bf16* k_raw, const wm
  *                    path) goes to finalize_stream, ordered after this step's
  *                    last attention only; every later call on the ring that
  *                    reads or writes the pool waits for it, so the next
- *                    step's RoPE overlaps it.
+ *                    step's RoPE overlaps it.  The append reads
+ *                    k[n_denoise-1] and v[n_denoise-1] on finalize_stream
+ *                    after this call returns: the caller keeps them
+ *                    unchanged and allocated until finalize_stream has
+ *                    passed this point (an event recorded there after the
+ *                    call marks it).
  * One-layer rings only (a model with L layers interleaves other work between
  * its layers: it calls wm_rope3d / wm_chunk_attn_layer per layer and one
  * wm_kvring_append_evict for all of them).
@@ -331,7 +339,8 @@ wm_status wm_rollout_step(wm_kvring* ring, int32_t n_denoise, const wm_bf16* con
  * (host and driver memory); the ring's pool and the tensors stay the
  * caller's.  wm_rollout_graph_destroy releases them; a graph must not
  * outlive its ring.
- * Errors: as wm_rollout_step; WM_E_STATE for a dead graph handle. */
+ * Errors: as wm_rollout_step; WM_E_STATE for a dead graph handle or once
+ * the graph's ring has been destroyed. */
 wm_status wm_rollout_graph_create(wm_kvring* ring, int32_t n_denoise, const wm_bf16* const* q,
                                   const wm_bf16* const* k, const wm_bf16* const* v,
                                   int32_t n_frames, const uint8_t* active, wm_bf16* q_rot_scratch,

@@ -231,6 +231,29 @@ def test_invalid_descriptor(bad):
     assert L.wm_last_error()
 
 
+def test_32bit_offset_limits():
+    """A rollout's K half and chunk tensor must stay below 2^31 elements (the
+    kernels form offsets within them in 32 bits): exactly 2^31 is refused,
+    one slot or frame fewer is accepted."""
+    L = wm.lib()
+    ft_128 = dict(frame_h=128, frame_w=128, head_dim=128)          # Ft = 2^14
+    # K half: (S+W) * Hkv * Ft * d = 128 * 8 * 2^14 * 128 = 2^31
+    at = make_desc(n_q_heads=8, n_kv_heads=8, n_sink=1, window=127, max_chunk=1, **ft_128)
+    below = make_desc(n_q_heads=8, n_kv_heads=8, n_sink=1, window=126, max_chunk=1, **ft_128)
+    # chunk tensor: C * Ft * Hq * d = 16 * 2^14 * 64 * 128 = 2^31
+    c_at = make_desc(n_q_heads=64, n_kv_heads=64, n_sink=1, window=3, max_chunk=16, **ft_128)
+    c_below = make_desc(n_q_heads=64, n_kv_heads=64, n_sink=1, window=3, max_chunk=15, **ft_128)
+    for d in (at, c_at):
+        assert L.wm_kvring_pool_bytes(ctypes.byref(d)) == 0
+        assert b"2^31" in L.wm_last_error()
+    for d in (below, c_below):
+        assert L.wm_kvring_pool_bytes(ctypes.byref(d)) > 0
+    # four 44x80 views, 16 kv heads, a 100-frame window: 2.9e9 elements
+    big = make_desc(n_q_heads=16, n_kv_heads=16, frame_h=44, frame_w=80, n_views=4, n_sink=1,
+                    window=100, max_chunk=1)
+    assert L.wm_kvring_pool_bytes(ctypes.byref(big)) == 0
+
+
 def test_create_argument_errors():
     L = wm.lib()
     d = make_desc()

@@ -121,3 +121,27 @@ def _run(wl, split):
     graph.close()
     for r in (eager, graphed, overl):
         r.close()
+
+
+def test_graph_of_a_destroyed_ring_is_refused():
+    """A graph whose ring was destroyed must not launch, also when a new ring
+    happens to be created at the same host address."""
+    wl = CASES["mha_c2"]
+    C, D = wl.chunk, wl.n_denoise
+    ring = new_ring(wl)
+    shape_q = (1, C * wl.ft, wl.n_q_heads, wl.head_dim)
+    shape_k = (1, C * wl.ft, wl.n_kv_heads, wl.head_dim)
+    gq = [torch.zeros(shape_q, dtype=torch.bfloat16, device="cuda") for _ in range(D)]
+    gk = [torch.zeros(shape_k, dtype=torch.bfloat16, device="cuda") for _ in range(D)]
+    gv = [torch.zeros(shape_k, dtype=torch.bfloat16, device="cuda") for _ in range(D)]
+    graph = ring.rollout_graph(gq, gk, gv, C)
+    graph.launch()
+    torch.cuda.synchronize()
+    ring.close()
+    others = [new_ring(wl) for _ in range(4)]   # one may reuse the freed address
+    with pytest.raises(wm.WMError) as e:
+        graph.launch()
+    assert e.value.name == "WM_E_STATE"
+    graph.close()
+    for r in others:
+        r.close()

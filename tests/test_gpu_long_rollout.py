@@ -16,6 +16,8 @@ mod 17), so the oracle can rebuild any frame.  Checked:
   retained frame of every rollout, for kv heads 0, 7 and 15.
 """
 
+import gc
+
 import numpy as np
 import pytest
 import torch
@@ -123,8 +125,12 @@ def test_long_rollout_10000_frames_bounded_and_exact():
             else:
                 assert reps[b] == {"written": [], "evicted": []}, (g, b)
         if g == mark_step:
+            # cyclic garbage (of this or earlier tests) is freed first, so
+            # that only this rollout's own memory is compared
+            gc.collect()
             torch.cuda.synchronize()
             mem_mark = (torch.cuda.memory_allocated(), torch.cuda.mem_get_info()[0])
+    gc.collect()
     torch.cuda.synchronize()
     assert n_checked == len(CHECK_ROLLOUTS) * len(CHECK_FRAMES) * D
     assert (torch.cuda.memory_allocated(), torch.cuda.mem_get_info()[0]) == mem_mark

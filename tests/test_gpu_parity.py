@@ -370,7 +370,7 @@ def test_rope_pair_equals_two_single_launches(d, hq, hkv, views):
 # ---------------------------------------------------------------------------
 # full-size workloads, steady state, sampled outputs
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("cfg", [2, 3, 4])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 6])
 def test_full_size_steady_state_sampled(cfg):
     """Window full, one chunk's denoise step at full size: RoPE bit-exact on the
     whole chunk, attention on sampled query rows and heads, then the append."""
@@ -391,8 +391,7 @@ def test_full_size_steady_state_sampled(cfg):
     q_np = src.batch_chunk([n0], n, 0, "q")
     k_np = src.batch_chunk([n0], n, 0, "k")
     v_np = src.batch_chunk([n0], n, 0, "v")
-    q_rot = ring.rope3d(dev(q_np), n)
-    k_rot = ring.rope3d(dev(k_np), n)
+    q_rot, k_rot = ring.rope3d_pair(dev(q_np), dev(k_np), n)   # as in the rollout step
     ws = workspace_for(ring, n)
     out = host(ring.chunk_attn(q_rot, k_rot, dev(v_np), n, workspace=ws))
     ref_q = ro.rope(q_np[0], n)

@@ -150,3 +150,18 @@ def test_refused_launch_mid_step_then_reset(kind, monkeypatch):
             assert reps[b] == {"written": written, "evicted": evicted}
         seq += C
     ring.close()
+
+
+def test_rope_tensor_size_limit_on_a_device_ring():
+    """wm_rope3d takes its own head count: a tensor of 2^31 elements or more
+    per rollout (32-bit offsets in the kernel) is refused before any launch."""
+    import ctypes
+    ring = wm.KVRing(1, 8, 8, 128, 256, 256, 1, 1, 1)   # Ft = 2^16
+    L = wm.lib()
+    buf = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    p = ctypes.c_void_p(buf.data_ptr())
+    assert L.wm_rope3d(ring._h, p, p, 256, 1, None, None, None) == 2    # 2^16 * 256 * 128 = 2^31
+    assert b"2^31" in L.wm_last_error()
+    assert L.wm_rope3d_pair(ring._h, p, p, 8, p, p, 256, 1, None, None, None) == 2
+    torch.cuda.synchronize()
+    ring.close()
