@@ -54,14 +54,26 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text):
+    """C/C++ source without comments and with whitespace runs collapsed (string
+    literals are left alone: the kernel sources hold no comment markers in
+    strings)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest():
-    """sha256 over the kernel sources, the internal header and the build flags."""
+    """sha256 over the code of the kernel sources and the internal header
+    (comments and layout ignored: they do not change the compiled kernels)
+    and over the build script, which holds the compile flags."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "autoregressive_video_world_amd", "csrc")
     for rel in ("kernels/chunk_attn.hip", "kernels/rope_append.hip", "wm_internal.hpp"):
-        with open(os.path.join(csrc, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(csrc, rel)) as f:
+            h.update(_code_only(f.read()).encode())
     with open(os.path.join(ROOT, "autoregressive_video_world_amd", "_build.py"), "rb") as f:
         h.update(f.read())
     return h.hexdigest()
@@ -275,6 +287,21 @@ def main():
     attn = lambda: ring.chunk_attn(q_rot, k_rot, vs[0], C, out=outs[0], workspace=ws)
     busy = lambda: torch.cuda._sleep(2_500_000)
     attn_mean, _ = timed(attn, args.kernel_reps)
+
+    # Spread of single launches: an event pair around each, back to back.
+    def per_launch(fn, reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        heat()
+        ev[0].record(stream)
+        for i in range(reps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+
+    attn_each = per_launch(attn, args.kernel_reps)
+    attn_p50 = attn_each[len(attn_each) // 2]
+    attn_p90 = attn_each[min(len(attn_each) - 1, (9 * len(attn_each)) // 10)]
     rope_mean, rope_host_us = timed(lambda: ring.rope3d_pair(qs[0], ks[0], C, y=q_rot, y2=k_rot),
                                     args.kernel_reps, busy)
     rope_q_mean, _ = timed(lambda: ring.rope3d(qs[0], C, y=q_rot), args.kernel_reps, busy)
@@ -426,7 +453,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "chunk_attn_kernel<128>",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": prof_traffic,
-                     "launch_ms_mean": round(attn_mean, 4),
+                     "launch_ms_mean": round(attn_mean, 4), "launch_ms_p50": round(attn_p50, 4),
+                     "launch_ms_p90": round(attn_p90, 4),
                      "flops_per_launch": wl.attn_flops(), "split_workspace_bytes": ws_bytes},
         "append": {"bound": "hbm", "achieved": round(app_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": round(app_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": app_bytes,

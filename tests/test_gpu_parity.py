@@ -413,3 +413,33 @@ def test_full_size_steady_state_sampled(cfg):
     for f, slot, t in ro.retained()[-n:]:
         assert np.array_equal(pk[0, slot], ro.cache[f][0].transpose(1, 0, 2))
     ring.close()
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_two_runs_bit_identical(split, monkeypatch):
+    """Determinism: the same rollout on two rings from the same seeded inputs
+    gives bit-identical outputs at every denoise step and identical pool
+    bytes, the key-range split and its combine included."""
+    wl = W(160, batch=2, n_q_heads=8, n_kv_heads=2, frame_h=9, frame_w=11, chunk=2, window=3,
+           n_gen=10, n_denoise=2)
+    if split:
+        monkeypatch.setenv("WM_ATTN_SPLIT", "3")
+    src = Source(wl)
+    B, C, D = wl.batch, wl.chunk, wl.n_denoise
+    rings = [make_ring(wl)[0] for _ in range(2)]
+    wss = [workspace_for(r, C) for r in rings]
+    if split:
+        assert all(w is not None for w in wss)
+    for ci in range(wl.n_gen // C):
+        n0 = ci * C
+        qs = [dev(src.batch_chunk([n0] * B, C, s, "q")) for s in range(D)]
+        ks = [dev(src.batch_chunk([n0] * B, C, s, "k")) for s in range(D)]
+        vs = [dev(src.batch_chunk([n0] * B, C, s, "v")) for s in range(D)]
+        runs = [r.rollout_step(qs, ks, vs, C, workspace=w) for r, w in zip(rings, wss)]
+        assert runs[0][1] == runs[1][1], ci
+        for s in range(D):
+            assert torch.equal(runs[0][0][s], runs[1][0][s]), (ci, s)
+    torch.cuda.synchronize()
+    assert torch.equal(rings[0].pool, rings[1].pool)
+    for r in rings:
+        r.close()
