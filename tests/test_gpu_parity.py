@@ -190,6 +190,43 @@ CASES = {
 }
 
 
+def sweep_cases(n=40, seed=2026):
+    """Seeded configurations across the features at once: batch and
+    staggered starts, d, GQA group, frame shape (down to 1x1), views, chunk,
+    sinks, window (0 included), prefill, denoise steps; each with the rollout
+    step or separate calls, and a forced key split where the keys span at
+    least two tiles.  Sizes stay small enough for the oracle."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        batch = int(rng.integers(1, 4))
+        hkv = int(rng.integers(1, 4))
+        group = int(rng.choice([1, 2, 4]))
+        views = int(rng.choice([1, 1, 2, 3]))
+        fh, fw = int(rng.integers(1, 10)), int(rng.integers(1, 14))
+        if views * fh * fw > 120 or hkv * group > 8:
+            continue
+        chunk = int(rng.integers(1, 5))
+        wl = W(1000 + len(out), batch=batch, n_q_heads=hkv * group, n_kv_heads=hkv,
+               head_dim=int(rng.choice([64, 128])), frame_h=fh, frame_w=fw, n_views=views, chunk=chunk,
+               n_sink=int(rng.integers(0, 3)), window=int(rng.integers(0, 6)),
+               prefill=int(rng.integers(0, 2)), n_gen=chunk * int(rng.integers(2, 4)) + int(rng.integers(0, chunk)),
+               n_denoise=int(rng.integers(1, 3)), stagger=int(rng.integers(0, 3)) if batch > 1 else 0)
+        split = bool(rng.integers(0, 2)) and (wl.n_sink + wl.window + chunk) * wl.ft >= 130
+        out.append((wl, bool(rng.integers(0, 2)), split))
+    return out
+
+
+SWEEP = sweep_cases()
+
+
+@pytest.mark.parametrize("i", range(len(SWEEP)))
+def test_rollout_parity_sweep(i):
+    wl, use_step, split = SWEEP[i]
+    print("sweep", i, wl, "use_step", use_step, "split", split, flush=True)
+    run_case(wl, use_step=use_step, split=split)
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_rollout_parity(name):
     print("case", name, flush=True)
