@@ -49,23 +49,67 @@ CASES = {
 
 def make_ring(wl, L):
     meta = wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
-                     wl.n_sink, wl.window, wl.chunk, meta_only=True, n_layers=L)
+                     wl.n_sink, wl.window, wl.chunk, meta_only=True, n_layers=L, n_views=wl.n_views)
     pool = torch.full((meta.pool_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
     meta.close()
     return wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
-                     wl.n_sink, wl.window, wl.chunk, pool=pool, n_layers=L)
+                     wl.n_sink, wl.window, wl.chunk, pool=pool, n_layers=L, n_views=wl.n_views)
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_multilayer_rollout_parity(name):
     wl, L = CASES[name]
     print("case", name, flush=True)
+    run_layers(wl, L)
+
+
+def layer_sweep(n=16, seed=2027):
+    """Seeded multi-layer configurations: 2-5 layers with views, GQA, d,
+    chunks, windows, staggered batches and a forced key split."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        hkv, group = int(rng.integers(1, 3)), int(rng.choice([1, 2, 4]))
+        views, fh, fw = int(rng.choice([1, 2])), int(rng.integers(1, 9)), int(rng.integers(1, 12))
+        if views * fh * fw > 96:
+            continue
+        chunk, batch = int(rng.integers(1, 4)), int(rng.integers(1, 3))
+        wl = W(2000 + len(out), batch=batch, n_q_heads=hkv * group, n_kv_heads=hkv,
+               head_dim=int(rng.choice([64, 128])), frame_h=fh, frame_w=fw, n_views=views, chunk=chunk,
+               n_sink=int(rng.integers(0, 3)), window=int(rng.integers(0, 5)),
+               prefill=int(rng.integers(0, 2)), n_gen=chunk * int(rng.integers(2, 4)),
+               n_denoise=int(rng.integers(1, 3)), stagger=int(rng.integers(0, 2)) if batch > 1 else 0)
+        split = bool(rng.integers(0, 2)) and (wl.n_sink + wl.window + chunk) * wl.ft >= 130
+        out.append((wl, int(rng.integers(2, 6)), split))
+    return out
+
+
+LAYER_SWEEP = layer_sweep()
+
+
+@pytest.mark.parametrize("i", range(len(LAYER_SWEEP)))
+def test_multilayer_parity_sweep(i, monkeypatch):
+    wl, L, split = LAYER_SWEEP[i]
+    print("layer sweep", i, wl, "layers", L, "split", split, flush=True)
+    if split:
+        monkeypatch.setenv("WM_ATTN_SPLIT", "3")
+    run_layers(wl, L, split)
+
+
+def run_layers(wl, L, split=False):
+    """Every layer's RoPE and attention against its own oracle; one append
+    for all layers; pool bytes per layer bit-exact, untouched slots keep the
+    sentinel."""
     B = wl.batch
     srcs = [Source(dataclasses.replace(wl, cfg=wl.cfg * 100 + l)) for l in range(L)]
     ring = make_ring(wl, L)
     assert ring.pool_bytes > 0
+    ws_bytes = ring.workspace_bytes(wl.chunk) if split else 0
+    if split:
+        assert ws_bytes > 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
     oracles = [[Rollout(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
-                        wl.n_sink, wl.window) for _ in range(B)] for _ in range(L)]
+                        wl.n_sink, wl.window, n_views=wl.n_views) for _ in range(B)] for _ in range(L)]
     actions = [([("prefill", wl.prefill)] if wl.prefill else []) + [("gen", c) for c in wl.chunks()]
                for _ in range(B)]
     used = [set() for _ in range(B)]
@@ -91,7 +135,7 @@ def test_multilayer_rollout_parity(name):
                     v_np = srcs[l].batch_chunk(n0s, n, s, "v")
                     q_rot = ring.rope3d(dev(q_np), n, active=active)
                     k_rot = ring.rope3d(dev(k_np), n, active=active)
-                    out = ring.chunk_attn(q_rot, k_rot, dev(v_np), n, active=active, layer=l)
+                    out = ring.chunk_attn(q_rot, k_rot, dev(v_np), n, active=active, layer=l, workspace=ws)
                     qr, kr, o = host(q_rot), host(k_rot), host(out)
                     for b in bs:
                         ref_q, ref_k, ref_o = oracles[l][b].denoise_step(q_np[b], k_np[b], v_np[b], n)
