@@ -43,8 +43,10 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=12, help="q heads in the oracle sample")
     ap.add_argument("--layers", type=int, default=30,
                     help="layers of the multi-layer append measurement (0 = skip)")
-    ap.add_argument("--views-workload", type=int, default=6,
-                    help="multi-view workload whose steady-state attention is also timed (0 = skip)")
+    ap.add_argument("--extra-workloads", default="3,4,6",
+                    help="comma-separated workload ids whose steady-state attention is also timed "
+                         "(0 = none): drive, the 32/8-head GQA workload (key-range split and "
+                         "combine) and the four-view workload by default")
     ap.add_argument("--modes-workload", type=int, default=1,
                     help="second workload whose rollout step is timed eager / finalize stream / graph "
                          "(0: none)")
@@ -380,29 +382,36 @@ def main():
         mring.close()
     torch.cuda.synchronize()
 
-    # Steady-state attention of a multi-view workload (several camera views
-    # per frame, attended jointly): same kernel, larger frames.
-    views = None
-    if args.views_workload and args.views_workload != args.workload:
-        vw = WORKLOADS[args.views_workload]
+    # Steady-state attention of other workloads: the same kernel at other
+    # shapes, the key-range split and its combine where the grid is small
+    # (launch time = attention + combine), several camera views per frame.
+    extras = []
+    for wid in [int(x) for x in args.extra_workloads.split(",") if x.strip()]:
+        if wid in (0, args.workload):
+            continue
+        vw = WORKLOADS[wid]
+        if vw.batch != 1:
+            continue
         vring = wm.KVRing(1, vw.n_q_heads, vw.n_kv_heads, vw.head_dim, vw.frame_h, vw.frame_w,
                           vw.n_sink, vw.window, vw.chunk, device=dev, n_views=vw.n_views)
         for _ in range(vw.n_sink + vw.window):
             vring.append_evict(randn(1, vw.ft, vw.n_kv_heads, vw.head_dim),
                                randn(1, vw.ft, vw.n_kv_heads, vw.head_dim), 1)
-        vq = vring.rope3d(randn(1, vw.nq, vw.n_q_heads, vw.head_dim), vw.chunk)
-        vk = vring.rope3d(randn(1, vw.nq, vw.n_kv_heads, vw.head_dim), vw.chunk)
+        vq, vk = vring.rope3d_pair(randn(1, vw.nq, vw.n_q_heads, vw.head_dim),
+                                   randn(1, vw.nq, vw.n_kv_heads, vw.head_dim), vw.chunk)
         vv = randn(1, vw.nq, vw.n_kv_heads, vw.head_dim)
         vo = torch.empty_like(vq)
         vws_bytes = vring.workspace_bytes(vw.chunk)
         vws = torch.empty(vws_bytes, dtype=torch.uint8, device=dev) if vws_bytes else None
-        v_mean, _ = timed(lambda: vring.chunk_attn(vq, vk, vv, vw.chunk, out=vo, workspace=vws), 3)
-        views = {"workload": "%s: %d q/%d kv heads, d %d, %d views of %dx%d tokens/frame (Nq %d, Nk %d)"
-                             % (vw.name, vw.n_q_heads, vw.n_kv_heads, vw.head_dim, vw.n_views, vw.frame_h,
-                                vw.frame_w, vw.nq, vw.steady_keys()),
-                 "attn_tflops": round(vw.attn_flops() / (v_mean * 1e-3) / 1e12, 2),
-                 "attn_pct_mfma_peak": round(100 * vw.attn_flops() / (v_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-                 "launch_ms_mean": round(v_mean, 3)}
+        reps = max(3, int(round(20 * 1e12 / vw.attn_flops())))   # about 20 ms of work
+        v_mean, _ = timed(lambda: vring.chunk_attn(vq, vk, vv, vw.chunk, out=vo, workspace=vws), reps)
+        tf = vw.attn_flops() / (v_mean * 1e-3) / 1e12
+        extras.append({"workload": "%s: %d q/%d kv heads, d %d, %s%dx%d tokens/frame (Nq %d, Nk %d)"
+                                   % (vw.name, vw.n_q_heads, vw.n_kv_heads, vw.head_dim,
+                                      "%d views of " % vw.n_views if vw.n_views > 1 else "", vw.frame_h,
+                                      vw.frame_w, vw.nq, vw.steady_keys()),
+                       "attn_tflops": round(tf, 2), "attn_pct_mfma_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                       "launch_ms_mean": round(v_mean, 4), "split_workspace_bytes": vws_bytes})
         vring.close()
         del vq, vk, vv, vo, vws
 
@@ -465,7 +474,7 @@ def main():
                    "copy_same_bytes_from_hbm": round(copy_cold_gbs, 1)},
         "rollout_modes": [modes] + ([modes_small] if modes_small else []),
         "append_layers": layers,
-        "views": views,
+        "other_workloads": extras,
         "rope": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
                  "launch_ms_mean": round(rope_mean, 5), "host_us_per_call": round(rope_host_us, 1),
