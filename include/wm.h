@@ -37,7 +37,9 @@
  *    rollout has a row block, active or not).
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every launch of a
  *    call goes onto that stream; no call synchronizes the device or copies
- *    device data to the host (wm_kvring_create aside).
+ *    device data to the host, with two exceptions: wm_kvring_create (a
+ *    synchronous table upload) and the replacement or destruction of a
+ *    rollout graph, which first waits for that graph's last launch.
  *  - The library allocates no device memory.  The caller owns the pool, all
  *    tensors, workspaces, host report/view structs and streams.
  *  - Errors: every argument is validated before anything is enqueued.  A
@@ -191,10 +193,10 @@ wm_status wm_kvring_view(const wm_kvring* ring, int32_t b, wm_ring_view* out);
  * frame j of rollout b sits at t = t_first[b] + j and, within its view,
  * h = (r mod frame_h*frame_w) / frame_w, w = r mod frame_w (every view has
  * its own grid; views of one frame share t); t_first == NULL means each
- * rollout's next uncommitted
- * frame (t0 + n_committed).  Bands [t | h | w] of the head dim; in a band of
- * width d_a, pair j = elements (2j, 2j+1) rotated by angle pos*theta^(-2j/d_a);
- * cos/sin are libm fp64 values rounded once to fp32 (computed on the host);
+ * rollout's next uncommitted frame (t0 + n_committed).  Bands [t | h | w] of
+ * the head dim; in a band of width d_a, pair j = elements (2j, 2j+1) rotated
+ * by angle pos*theta^(-2j/d_a); cos/sin are libm fp64 values rounded once to
+ * fp32 (computed on the host);
  * y0 = x0*c - x1*s, y1 = x0*s + x1*c in fp64 (the products are exact), then
  * rounded to bf16 round-to-nearest-even.  Only active rollouts (active[b] !=
  * 0; NULL = all) are read or written.
@@ -333,14 +335,16 @@ wm_status wm_rollout_step(wm_kvring* ring, int32_t n_denoise, const wm_bf16* con
  * into the graph's nodes and launches the graph on `stream`, then commits
  * the append like wm_kvring_append_evict.  When the planned launches differ
  * in kernel or grid from the graph's (the window still filling, a different
- * key split), the graph is first rebuilt for them; *rebuilt (may be NULL) is
- * 1 then.  Results are those of wm_rollout_step either way.
+ * key split), the graph is first rebuilt for them, after its previous launch
+ * has finished (the host waits for it); *rebuilt (may be NULL) is 1 then.
+ * Results are those of wm_rollout_step either way.
  * The graph and its executable instance are HIP objects the library creates
  * (host and driver memory); the ring's pool and the tensors stay the
- * caller's.  wm_rollout_graph_destroy releases them; a graph must not
- * outlive its ring.
- * Errors: as wm_rollout_step; WM_E_STATE for a dead graph handle or once
- * the graph's ring has been destroyed. */
+ * caller's.  wm_rollout_graph_destroy waits for the graph's last launch and
+ * releases them.  Once its ring is destroyed a graph can only be destroyed.
+ * Errors: as wm_rollout_step (create and launch: WM_E_HIP for a failed graph
+ * call); WM_E_STATE for a dead graph handle or, at launch, once the graph's
+ * ring has been destroyed. */
 wm_status wm_rollout_graph_create(wm_kvring* ring, int32_t n_denoise, const wm_bf16* const* q,
                                   const wm_bf16* const* k, const wm_bf16* const* v,
                                   int32_t n_frames, const uint8_t* active, wm_bf16* q_rot_scratch,
