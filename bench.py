@@ -133,10 +133,59 @@ def cpu_baseline(wl, n_heads):
     except Exception:
         pass
     cores = threads or len(os.sched_getaffinity(0))
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join("%s %s (%s threads)" % (i.get("internal_api"), i.get("version"), i.get("num_threads"))
+                         for i in threadpool_info() if i.get("user_api") == "blas") or None
+    except Exception:
+        pass
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": "one steady-state denoise step of %s (RoPE of the chunk's Q and K, attention "
                       "of all %d queries over %d keys) for %d of %d q heads, fp64 NumPy; %.1f s"
-                      % (wl.name, wl.nq, wl.steady_keys(), len(heads), wl.n_q_heads, dt)}
+                      % (wl.name, wl.nq, wl.steady_keys(), len(heads), wl.n_q_heads, dt),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model, "blas": blas}
+
+
+def whole_rollout(torch, wm, wl, dev, qs, ks, vs, outs, q_rot, k_rot, heat, reps=3):
+    """A whole rollout from an empty ring (prefill, then every chunk, the
+    window filling on the way): algorithmic attention flops of all steps /
+    wall time of the whole loop, the median of `reps` rollouts, each after
+    `heat` has brought the clock to its sustained level."""
+    C, D, ft = wl.chunk, wl.n_denoise, wl.ft
+    R = wl.n_sink + wl.window
+    times, flops = [], 0.0
+    for _ in range(reps):
+        ring = wm.KVRing(1, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                         wl.n_sink, wl.window, C, device=dev, n_views=wl.n_views)
+        ws_bytes = ring.workspace_bytes(C)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+        views = {c: ([q[:, :c * ft] for q in qs], [k[:, :c * ft] for k in ks], [v[:, :c * ft] for v in vs],
+                     [o[:, :c * ft] for o in outs], q_rot[:, :c * ft], k_rot[:, :c * ft])
+                 for c in set(wl.chunks())}
+        heat()
+        t0 = time.perf_counter()
+        committed, flops = 0, 0.0
+        if wl.prefill:
+            ring.append_evict(ks[-1][:, :wl.prefill * ft], vs[-1][:, :wl.prefill * ft], wl.prefill)
+            committed = wl.prefill
+        for c in wl.chunks():
+            q, k, v, o, qr, kr = views[c]
+            ring.rollout_step(q, k, v, c, outs=o, q_rot_scratch=qr, k_rot_scratch=kr, workspace=ws)
+            flops += D * wl.attn_flops(n_q=c * ft, n_k=(min(committed, R) + c) * ft)
+            committed += c
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+        ring.close()
+    t = sorted(times)[len(times) // 2]
+    return {"frames": wl.prefill + wl.n_gen, "chunks": len(wl.chunks()), "ms": round(t * 1e3, 3),
+            "attn_tflops": round(flops / t / 1e12, 2)}
 
 
 def rollout_modes(torch, wm, wl, randn, dev, steps, warmup, ring=None):
@@ -239,6 +288,12 @@ def main():
         ring.rollout_step(qs, ks, vs, C, outs=outs, q_rot_scratch=q_rot, k_rot_scratch=k_rot,
                           workspace=ws)
 
+    # The first call (code-object load, first-touch of the buffers) on its own.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    first_step_ms = (time.perf_counter() - t0) * 1e3
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -415,6 +470,9 @@ def main():
         vring.close()
         del vq, vk, vv, vo, vws
 
+    # Whole-rollout average beside the steady state.
+    rollout = whole_rollout(torch, wm, wl, dev, qs, ks, vs, outs, q_rot, k_rot, heat)
+
     # The same step launched from the finalize stream and from a HIP graph,
     # here and on a workload small enough that launch costs show.
     modes = {"workload": wl.name, **rollout_modes(torch, wm, wl, randn, dev, args.steps,
@@ -458,6 +516,8 @@ def main():
                    "batch": 1, "n_q": wl.nq, "n_k": wl.steady_keys(), "denoise_steps": D},
         "denoise_steps_per_s_per_chunk": round(1e3 / (attn_mean + rope_mean), 2),
         "chunks_per_s": round(1e3 / ms_per_step, 3),
+        "first_step_ms": round(first_step_ms, 3),
+        "whole_rollout": rollout,
         "attn_pct_mfma_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "kernel": "chunk_attn_kernel<128>",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
