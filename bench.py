@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--modes-workload", type=int, default=1,
                     help="second workload whose rollout step is timed eager / finalize stream / graph "
                          "(0: none)")
+    ap.add_argument("--steady-only", action="store_true",
+                    help="time only the steady-state step and its kernels (no multi-layer append, "
+                         "extra workloads, launch modes or whole rollout): every attention launch "
+                         "then has the steady shape, as profiling runs want")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain elementwise copy of this many MiB first (untimed), as the "
                          "known-size reference for HBM byte counters")
@@ -233,6 +237,8 @@ def rollout_modes(torch, wm, wl, randn, dev, steps, warmup, ring=None):
 
 def main():
     args = parse()
+    if args.steady_only:
+        args.layers, args.extra_workloads, args.modes_workload = 0, "0", 0
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (it would shard by rollout "
               "or by kv head with no collective in the path); run with --gpus 1", file=sys.stderr)
@@ -471,12 +477,13 @@ def main():
         del vq, vk, vv, vo, vws
 
     # Whole-rollout average beside the steady state.
-    rollout = whole_rollout(torch, wm, wl, dev, qs, ks, vs, outs, q_rot, k_rot, heat)
+    rollout = None if args.steady_only else whole_rollout(torch, wm, wl, dev, qs, ks, vs, outs,
+                                                            q_rot, k_rot, heat)
 
     # The same step launched from the finalize stream and from a HIP graph,
     # here and on a workload small enough that launch costs show.
-    modes = {"workload": wl.name, **rollout_modes(torch, wm, wl, randn, dev, args.steps,
-                                                  args.warmup, ring)}
+    modes = None if args.steady_only else {
+        "workload": wl.name, **rollout_modes(torch, wm, wl, randn, dev, args.steps, args.warmup, ring)}
     modes_small = None
     if args.modes_workload and args.modes_workload != args.workload:
         mw = WORKLOADS[args.modes_workload]
@@ -532,7 +539,7 @@ def main():
                    "achieved_inputs_from_hbm": round(app_cold_gbs, 1),
                    "frac_inputs_from_hbm": round(app_cold_gbs / PEAK_HBM_GBS, 4),
                    "copy_same_bytes_from_hbm": round(copy_cold_gbs, 1)},
-        "rollout_modes": [modes] + ([modes_small] if modes_small else []),
+        "rollout_modes": ([modes] if modes else []) + ([modes_small] if modes_small else []),
         "append_layers": layers,
         "other_workloads": extras,
         "rope": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
