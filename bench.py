@@ -43,10 +43,11 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=12, help="q heads in the oracle sample")
     ap.add_argument("--layers", type=int, default=30,
                     help="layers of the multi-layer append measurement (0 = skip)")
-    ap.add_argument("--extra-workloads", default="3,4,6",
+    ap.add_argument("--extra-workloads", default="3,4,5,6",
                     help="comma-separated workload ids whose steady-state attention is also timed "
                          "(0 = none): drive, the 32/8-head GQA workload (key-range split and "
-                         "combine) and the four-view workload by default")
+                         "combine), eight drive rollouts in one call and the four-view workload "
+                         "by default")
     ap.add_argument("--modes-workload", type=int, default=1,
                     help="second workload whose rollout step is timed eager / finalize stream / graph "
                          "(0: none)")
@@ -451,24 +452,25 @@ def main():
         if wid in (0, args.workload):
             continue
         vw = WORKLOADS[wid]
-        if vw.batch != 1:
-            continue
-        vring = wm.KVRing(1, vw.n_q_heads, vw.n_kv_heads, vw.head_dim, vw.frame_h, vw.frame_w,
+        nb = vw.batch   # every rollout at steady state (window full), one call for all
+        vring = wm.KVRing(nb, vw.n_q_heads, vw.n_kv_heads, vw.head_dim, vw.frame_h, vw.frame_w,
                           vw.n_sink, vw.window, vw.chunk, device=dev, n_views=vw.n_views)
         for _ in range(vw.n_sink + vw.window):
-            vring.append_evict(randn(1, vw.ft, vw.n_kv_heads, vw.head_dim),
-                               randn(1, vw.ft, vw.n_kv_heads, vw.head_dim), 1)
-        vq, vk = vring.rope3d_pair(randn(1, vw.nq, vw.n_q_heads, vw.head_dim),
-                                   randn(1, vw.nq, vw.n_kv_heads, vw.head_dim), vw.chunk)
-        vv = randn(1, vw.nq, vw.n_kv_heads, vw.head_dim)
+            vring.append_evict(randn(nb, vw.ft, vw.n_kv_heads, vw.head_dim),
+                               randn(nb, vw.ft, vw.n_kv_heads, vw.head_dim), 1)
+        vq, vk = vring.rope3d_pair(randn(nb, vw.nq, vw.n_q_heads, vw.head_dim),
+                                   randn(nb, vw.nq, vw.n_kv_heads, vw.head_dim), vw.chunk)
+        vv = randn(nb, vw.nq, vw.n_kv_heads, vw.head_dim)
         vo = torch.empty_like(vq)
         vws_bytes = vring.workspace_bytes(vw.chunk)
         vws = torch.empty(vws_bytes, dtype=torch.uint8, device=dev) if vws_bytes else None
-        reps = max(3, int(round(20 * 1e12 / vw.attn_flops())))   # about 20 ms of work
+        flops = nb * vw.attn_flops()
+        reps = max(3, int(round(20 * 1e12 / flops)))   # about 20 ms of work
         v_mean, _ = timed(lambda: vring.chunk_attn(vq, vk, vv, vw.chunk, out=vo, workspace=vws), reps)
-        tf = vw.attn_flops() / (v_mean * 1e-3) / 1e12
-        extras.append({"workload": "%s: %d q/%d kv heads, d %d, %s%dx%d tokens/frame (Nq %d, Nk %d)"
-                                   % (vw.name, vw.n_q_heads, vw.n_kv_heads, vw.head_dim,
+        tf = flops / (v_mean * 1e-3) / 1e12
+        extras.append({"workload": "%s: %s%d q/%d kv heads, d %d, %s%dx%d tokens/frame (Nq %d, Nk %d)"
+                                   % (vw.name, "%d rollouts, " % nb if nb > 1 else "", vw.n_q_heads,
+                                      vw.n_kv_heads, vw.head_dim,
                                       "%d views of " % vw.n_views if vw.n_views > 1 else "", vw.frame_h,
                                       vw.frame_w, vw.nq, vw.steady_keys()),
                        "attn_tflops": round(tf, 2), "attn_pct_mfma_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
