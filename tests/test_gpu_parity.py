@@ -187,6 +187,10 @@ CASES = {
     "views4_gqa_d64": W(110, n_views=4, head_dim=64, n_q_heads=6, n_kv_heads=2, frame_h=5, frame_w=6,
                         window=2, prefill=1, n_gen=5),
     "views7_batch2": W(111, n_views=7, batch=2, frame_h=3, frame_w=5, window=2, n_gen=5, stagger=1),
+    # more rollouts than one attention launch takes (64): two launch groups,
+    # staggered admission, many RoPE and append launches per call
+    "batch70_two_groups": W(112, batch=70, n_q_heads=4, n_kv_heads=2, frame_h=3, frame_w=6, chunk=2,
+                            window=2, n_gen=4, n_denoise=2, stagger=0),
 }
 
 
