@@ -231,6 +231,27 @@ def test_rollout_parity_sweep(i):
     run_case(wl, use_step=use_step, split=split)
 
 
+# The descriptor's limits, with tiny frames so the oracle stays quick.
+LIMITS = {
+    # max_chunk = 16 (two RoPE row batches per rollout), a ragged last chunk
+    "chunk16": W(130, frame_h=2, frame_w=5, chunk=16, n_sink=1, window=3, n_gen=37, n_denoise=2),
+    # S + W = 256 slots, the window wrapping once
+    "ring256": W(131, n_q_heads=2, n_kv_heads=1, head_dim=64, frame_h=1, frame_w=2, n_sink=6,
+                 window=250, n_gen=260),
+    # a GQA group of 64 q heads on one kv head
+    "group64": W(132, n_q_heads=64, n_kv_heads=1, frame_h=3, frame_w=5, window=2, n_gen=4),
+    # 1024 rollouts: 16 attention launch groups per call
+    "batch1024": W(133, batch=1024, n_q_heads=2, n_kv_heads=1, head_dim=64, frame_h=1, frame_w=3,
+                   window=1, n_gen=2),
+}
+
+
+@pytest.mark.parametrize("name", list(LIMITS))
+def test_rollout_parity_at_limits(name):
+    print("limit case", name, flush=True)
+    run_case(LIMITS[name], use_step=name in ("chunk16", "batch1024"))
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_rollout_parity(name):
     print("case", name, flush=True)
