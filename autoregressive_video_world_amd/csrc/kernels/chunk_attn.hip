@@ -624,28 +624,43 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   if (idx >= rows * kCpr) return;
   const int c = (int)(idx % kCpr);
   const int64_t row = idx / kCpr;
-  float M = -INFINITY;
-  for (int s = 0; s < p.nsplit; ++s) {
-    const float l = p.part_ml[(s * rows + row) * 2 + 1];
-    if (l > 0.f) M = fmaxf(M, p.part_ml[(s * rows + row) * 2 + 0]);
+  // Every split's (max, sum) and output slice are loaded before any is used,
+  // so a thread waits for one round of memory latency, not two per split.
+  // A split with an empty key range has sum 0 and an unwritten output slice:
+  // its values are loaded but never used.
+  float m[kAttnMaxSplit], l[kAttnMaxSplit];
+  float4 a[kAttnMaxSplit], b[kAttnMaxSplit];
+#pragma unroll
+  for (int s = 0; s < kAttnMaxSplit; ++s) {
+    if (s < p.nsplit) {
+      const int64_t r = s * rows + row;
+      const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + r * 2);
+      m[s] = ml.x;
+      l[s] = ml.y;
+      const float4* src = reinterpret_cast<const float4*>(p.part_o + r * HD + c * 8);
+      a[s] = src[0];
+      b[s] = src[1];
+    }
   }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kAttnMaxSplit; ++s)
+    if (s < p.nsplit && l[s] > 0.f) M = fmaxf(M, m[s]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int s = 0; s < p.nsplit; ++s) {
-    const float l = p.part_ml[(s * rows + row) * 2 + 1];
-    if (!(l > 0.f)) continue;
-    const float w = l * __builtin_amdgcn_exp2f(p.part_ml[(s * rows + row) * 2 + 0] - M);
+#pragma unroll
+  for (int s = 0; s < kAttnMaxSplit; ++s) {
+    if (!(s < p.nsplit && l[s] > 0.f)) continue;
+    const float w = l[s] * __builtin_amdgcn_exp2f(m[s] - M);
     wsum += w;
-    const float4* src = reinterpret_cast<const float4*>(p.part_o + (s * rows + row) * HD + c * 8);
-    const float4 a = src[0], b = src[1];
-    acc[0] += w * a.x;
-    acc[1] += w * a.y;
-    acc[2] += w * a.z;
-    acc[3] += w * a.w;
-    acc[4] += w * b.x;
-    acc[5] += w * b.y;
-    acc[6] += w * b.z;
-    acc[7] += w * b.w;
+    acc[0] += w * a[s].x;
+    acc[1] += w * a[s].y;
+    acc[2] += w * a[s].z;
+    acc[3] += w * a[s].w;
+    acc[4] += w * b[s].x;
+    acc[5] += w * b[s].y;
+    acc[6] += w * b[s].z;
+    acc[7] += w * b[s].w;
   }
   const float inv = 1.0f / wsum;
   const int h = (int)(row % p.hq);

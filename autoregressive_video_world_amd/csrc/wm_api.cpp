@@ -488,7 +488,7 @@ wm_status do_append(wm_kvring* r, const wm_bf16* k_raw, const wm_bf16* v, int n_
 // 4*Nk*d flop of attention per row at ~1 PFLOP/s, i.e. ~400/Nk of the
 // attention time per split.  Each split keeps at least two 64-key tiles.
 constexpr int kCUs = 256;
-constexpr int kMaxSplit = 8;
+constexpr int kMaxSplit = wm::kAttnMaxSplit;
 
 // WM_ATTN_SPLIT=n (1..8) overrides the choice (tuning and tests); read on
 // every call.

@@ -78,6 +78,7 @@ LaunchSpec kv_append_spec(const RopeParams& p);
 // Chunk attention
 // ---------------------------------------------------------------------------
 constexpr int kAttnMaxB = 64;    // rollouts per launch
+constexpr int kAttnMaxSplit = 8; // key-range splits per attention launch
 
 struct AttnParams {
   const uint16_t* q;      // [B][Nq][Hq][d]
