@@ -12,6 +12,7 @@ first steady-state chunk is also checked against the fp64 oracle.
 """
 
 import os
+import time
 
 import numpy as np
 import pytest
@@ -28,6 +29,9 @@ CASES = {
     "mha_c2": Workload(401, "graph_mha", 1, 4, 4, 128, 10, 10, 2, 1, 3, 0, 14, 2),
     "gqa_batch2": Workload(402, "graph_gqa", 2, 8, 2, 128, 7, 9, 1, 1, 2, 0, 8, 2),
     "d64_c3": Workload(403, "graph_d64", 1, 2, 2, 64, 5, 10, 3, 1, 4, 0, 15, 1),
+    # a step of ~0.6 ms on the GPU against ~40 us of host time per launch:
+    # the host queues replays and refreshes parameters while earlier replays run
+    "long_steps": Workload(404, "graph_long", 1, 12, 12, 128, 30, 52, 1, 1, 18, 0, 40, 2),
 }
 
 
@@ -145,3 +149,45 @@ def test_graph_of_a_destroyed_ring_is_refused():
     graph.close()
     for r in others:
         r.close()
+
+
+@pytest.mark.parametrize("name", ["mha_c2", "gqa_batch2", "long_steps"])
+def test_back_to_back_graph_launches_match_eager(name):
+    """Graph launches queued back to back with no synchronization between
+    them (each refreshes its node parameters while the previous replay may
+    still run) give the same pool bytes and last outputs as eager steps."""
+    wl = CASES[name]
+    B, C, D = wl.batch, wl.chunk, wl.n_denoise
+    src = Source(wl)
+    eager, graphed = new_ring(wl), new_ring(wl)
+    shape_q = (B, C * wl.ft, wl.n_q_heads, wl.head_dim)
+    shape_k = (B, C * wl.ft, wl.n_kv_heads, wl.head_dim)
+    qs = [dev(src.batch_chunk([0] * B, C, s, "q")) for s in range(D)]
+    ks = [dev(src.batch_chunk([0] * B, C, s, "k")) for s in range(D)]
+    vs = [dev(src.batch_chunk([0] * B, C, s, "v")) for s in range(D)]
+    assert qs[0].shape == shape_q and ks[0].shape == shape_k
+    # fill the window first (shapes settle), then many steps without a sync
+    graph = graphed.rollout_graph(qs, ks, vs, C)
+    n_fill = -(-(wl.n_sink + wl.window) // C)
+    for _ in range(n_fill):
+        eager.rollout_step(qs, ks, vs, C)
+        graph.launch()
+    torch.cuda.synchronize()
+    outs_e = None
+    for _ in range(12):
+        outs_e, _ = eager.rollout_step(qs, ks, vs, C)
+    t0 = time.perf_counter()
+    for _ in range(12):
+        graph.launch()
+        assert not graph.rebuilt
+    queued = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    print("12 graph launches queued in %.2f ms, ran in %.2f ms" % (queued * 1e3, (time.perf_counter() - t0) * 1e3))
+    assert torch.equal(graphed.pool_k(), eager.pool_k()) and torch.equal(graphed.pool_v(), eager.pool_v())
+    for s in range(D):
+        assert torch.equal(graph.outs[s], outs_e[s]), s
+    for b in range(B):
+        assert graphed.view(b) == eager.view(b)
+    graph.close()
+    eager.close()
+    graphed.close()
