@@ -661,20 +661,21 @@ wm_status check_step(const wm_kvring* ring, int n_denoise, const wm_bf16* const*
 }
 
 // n_denoise x (RoPE of Q and K, attention), then, with `append`, the append
-// of the last step's K and V (bookkeeping advanced only with `commit`).  A
-// non-null wait_stream first orders the attentions after a pending finalize.
+// of the last step's K and V (bookkeeping advanced only with `commit`).
+// Launched directly, the first attention is ordered after a pending append on
+// a finalize stream (the null stream is a stream like any other here); a
+// recorded step leaves that to the graph launch.
 wm_status do_step(wm_kvring* ring, int n_denoise, const wm_bf16* const* q, const wm_bf16* const* k,
                   const wm_bf16* const* v, int n_frames, const uint8_t* active, wm_bf16* q_rot,
                   wm_bf16* k_rot, wm_bf16* const* out, void* ws, size_t ws_bytes,
-                  wm_append_report* rep, Sink& sink, bool append, hipStream_t wait_stream,
-                  bool commit = true) {
+                  wm_append_report* rep, Sink& sink, bool append, bool commit = true) {
   wm_status st;
   const wm_kvring_desc& d = ring->desc;
   for (int i = 0; i < n_denoise; ++i) {
     if ((st = do_rope(ring, q[i], q_rot, d.n_q_heads, n_frames, nullptr, active, sink, k[i], k_rot,
                       d.n_kv_heads)) != WM_OK)
       return st;
-    if (i == 0 && wait_stream && (st = wait_finalize(ring, wait_stream)) != WM_OK) return st;
+    if (i == 0 && !sink.rec && (st = wait_finalize(ring, sink.s)) != WM_OK) return st;
     if ((st = do_attn(ring, 0, q_rot, k_rot, v[i], n_frames, active, 0.f, out[i], ws, ws_bytes,
                       sink)) != WM_OK)
       return st;
@@ -692,7 +693,7 @@ wm_status plan_graph_step(wm_rollout_graph* g, std::vector<PLaunch>* plan, wm_ap
   plan->reserve(4 * g->D + 4);
   return do_step(g->ring, g->D, g->q.data(), g->k.data(), g->v.data(), g->n_frames,
                  g->has_active ? g->active.data() : nullptr, g->q_rot, g->k_rot, g->out.data(), g->ws,
-                 g->ws_bytes, reps, rec, true, nullptr, false);
+                 g->ws_bytes, reps, rec, true, false);
 }
 
 // A graph of the planned launches in one dependency chain, and its instance.
@@ -966,7 +967,7 @@ wm_status wm_rollout_step(wm_kvring* ring, int32_t n_denoise, const wm_bf16* con
   Sink main{s};
   if (!fs || fs == s) {
     st = do_step(ring, n_denoise, q, k, v, n_frames, active, q_rot_scratch, k_rot_scratch, out,
-                 workspace, workspace_bytes, rep, main, true, s);
+                 workspace, workspace_bytes, rep, main, true);
     if (st != WM_OK) return st;
     return finish(s);
   }
@@ -975,7 +976,7 @@ wm_status wm_rollout_step(wm_kvring* ring, int32_t n_denoise, const wm_bf16* con
   // finalize stream; the next call's pool accesses wait for it.
   if ((st = make_events(ring)) != WM_OK) return st;
   st = do_step(ring, n_denoise, q, k, v, n_frames, active, q_rot_scratch, k_rot_scratch, out,
-               workspace, workspace_bytes, rep, main, false, s);
+               workspace, workspace_bytes, rep, main, false);
   if (st != WM_OK) return st;
   hipError_t e = hipEventRecord(ring->ev_attn, s);
   if (e == hipSuccess) e = hipStreamWaitEvent(fs, ring->ev_attn, 0);

@@ -155,11 +155,15 @@ def test_graph_of_a_destroyed_ring_is_refused():
 def test_back_to_back_graph_launches_match_eager(name):
     """Graph launches queued back to back with no synchronization between
     them (each refreshes its node parameters while the previous replay may
-    still run) give the same pool bytes and last outputs as eager steps."""
+    still run), and steps whose appends go to a finalize stream -- on torch's
+    default stream, which reaches the library as the null stream -- give the
+    same pool bytes and last outputs as eager steps; so does a plain step
+    queued right after a finalize-stream step."""
     wl = CASES[name]
     B, C, D = wl.batch, wl.chunk, wl.n_denoise
     src = Source(wl)
-    eager, graphed = new_ring(wl), new_ring(wl)
+    eager, graphed, overl = new_ring(wl), new_ring(wl), new_ring(wl)
+    fin = torch.cuda.Stream()
     shape_q = (B, C * wl.ft, wl.n_q_heads, wl.head_dim)
     shape_k = (B, C * wl.ft, wl.n_kv_heads, wl.head_dim)
     qs = [dev(src.batch_chunk([0] * B, C, s, "q")) for s in range(D)]
@@ -172,22 +176,30 @@ def test_back_to_back_graph_launches_match_eager(name):
     for _ in range(n_fill):
         eager.rollout_step(qs, ks, vs, C)
         graph.launch()
+        overl.rollout_step(qs, ks, vs, C, finalize_stream=fin)
     torch.cuda.synchronize()
-    outs_e = None
+    outs_e = outs_o = None
     for _ in range(12):
         outs_e, _ = eager.rollout_step(qs, ks, vs, C)
-    t0 = time.perf_counter()
+    plain_e, _ = eager.rollout_step(qs, ks, vs, C)
     for _ in range(12):
+        outs_o, _ = overl.rollout_step(qs, ks, vs, C, finalize_stream=fin)
+    plain_o, _ = overl.rollout_step(qs, ks, vs, C)   # must wait for the last pending append
+    t0 = time.perf_counter()
+    for _ in range(13):
         graph.launch()
         assert not graph.rebuilt
     queued = time.perf_counter() - t0
     torch.cuda.synchronize()
-    print("12 graph launches queued in %.2f ms, ran in %.2f ms" % (queued * 1e3, (time.perf_counter() - t0) * 1e3))
-    assert torch.equal(graphed.pool_k(), eager.pool_k()) and torch.equal(graphed.pool_v(), eager.pool_v())
+    print("13 graph launches queued in %.2f ms, ran in %.2f ms" % (queued * 1e3, (time.perf_counter() - t0) * 1e3))
+    for r in (graphed, overl):
+        assert torch.equal(r.pool_k(), eager.pool_k()) and torch.equal(r.pool_v(), eager.pool_v())
+        for b in range(B):
+            assert r.view(b) == eager.view(b)
     for s in range(D):
-        assert torch.equal(graph.outs[s], outs_e[s]), s
-    for b in range(B):
-        assert graphed.view(b) == eager.view(b)
+        assert torch.equal(graph.outs[s], plain_e[s]), s
+        assert torch.equal(outs_o[s], outs_e[s]), s
+        assert torch.equal(plain_o[s], plain_e[s]), s
     graph.close()
-    eager.close()
-    graphed.close()
+    for r in (eager, graphed, overl):
+        r.close()
