@@ -203,3 +203,39 @@ def test_back_to_back_graph_launches_match_eager(name):
     graph.close()
     for r in (eager, graphed, overl):
         r.close()
+
+
+def test_graph_and_eager_steps_interleave_on_one_ring():
+    """Graph replays, eager steps and finalize-stream steps alternate on one
+    ring with no synchronization; every step's outputs and the final pool
+    equal those of eager steps only."""
+    wl = CASES["gqa_batch2"]
+    B, C, D = wl.batch, wl.chunk, wl.n_denoise
+    src = Source(wl)
+    ref, mixed = new_ring(wl), new_ring(wl)
+    fin = torch.cuda.Stream()
+    qs = [dev(src.batch_chunk([0] * B, C, s, "q")) for s in range(D)]
+    ks = [dev(src.batch_chunk([0] * B, C, s, "k")) for s in range(D)]
+    vs = [dev(src.batch_chunk([0] * B, C, s, "v")) for s in range(D)]
+    graph = mixed.rollout_graph(qs, ks, vs, C)
+    want, got = [], []
+    for i in range(15):
+        o, _ = ref.rollout_step(qs, ks, vs, C)
+        want.append([x.clone() for x in o])
+        kind = i % 3
+        if kind == 0:
+            graph.launch()
+            o = graph.outs
+        elif kind == 1:
+            o, _ = mixed.rollout_step(qs, ks, vs, C)
+        else:
+            o, _ = mixed.rollout_step(qs, ks, vs, C, finalize_stream=fin)
+        got.append([x.clone() for x in o])
+    torch.cuda.synchronize()
+    for i in range(15):
+        for s in range(D):
+            assert torch.equal(got[i][s], want[i][s]), (i, s)
+    assert torch.equal(mixed.pool_k(), ref.pool_k()) and torch.equal(mixed.pool_v(), ref.pool_v())
+    graph.close()
+    ref.close()
+    mixed.close()
