@@ -391,3 +391,37 @@ def test_refused_append_launch_keeps_bookkeeping(monkeypatch):
     v = r.view(1)
     assert [(f, t) for f, _, t in v["retained"]] == [(0, 50), (1, 51)] and v["t0"] == 50
     r.close()
+
+
+def test_rings_in_parallel_host_threads():
+    """Separate rings from separate host threads at once (ctypes releases the
+    GIL during the calls): the handle registry stays consistent, each ring's
+    bookkeeping is its own, and each thread reads its own last error."""
+    import threading
+    L = wm.lib()
+    errors = []
+
+    def worker(tid):
+        try:
+            for it in range(150):
+                S, W = 1 + tid % 3, 2 + it % 4
+                r = wm.KVRing(2, 4, 2, 128, 3, 4, S, W, 2, meta_only=True)
+                n = 1 + (tid + it) % 9
+                for _ in range(n):
+                    r.append_evict(None, None, 1)
+                v = r.view(0)
+                assert v["n_committed"] == n and len(v["retained"]) == min(n, S + W), (tid, it)
+                # a failing call: this thread's message, not another's
+                bad = "rollout %d out of range" % (7 + tid)
+                assert L.wm_kvring_reset(r._h, 7 + tid, 0) == 1
+                assert L.wm_last_error().decode() == bad, (tid, L.wm_last_error())
+                r.close()
+        except Exception as e:   # reported to the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
