@@ -239,3 +239,40 @@ def test_graph_and_eager_steps_interleave_on_one_ring():
     graph.close()
     ref.close()
     mixed.close()
+
+
+def test_created_stream_and_graph_with_active_mask():
+    """A rollout on a created (non-default) stream, and a graph built with an
+    active mask (rollout 1 idle), against eager steps on the default stream
+    with the same mask: outputs of the active rollout, reports and pools are
+    identical, and the idle rollout's slots stay as they were."""
+    wl = CASES["gqa_batch2"]
+    B, C, D = wl.batch, wl.chunk, wl.n_denoise
+    src = Source(wl)
+    ref, on_stream, graphed = new_ring(wl), new_ring(wl), new_ring(wl)
+    qs = [dev(src.batch_chunk([0] * B, C, s, "q")) for s in range(D)]
+    ks = [dev(src.batch_chunk([0] * B, C, s, "k")) for s in range(D)]
+    vs = [dev(src.batch_chunk([0] * B, C, s, "v")) for s in range(D)]
+    active = [1, 0]
+    graph = graphed.rollout_graph(qs, ks, vs, C, active=active)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())   # the inputs were made on the default stream
+    for i in range(9):
+        o_ref, rep_ref = ref.rollout_step(qs, ks, vs, C, active=active)
+        with torch.cuda.stream(side):
+            o_side, rep_side = on_stream.rollout_step(qs, ks, vs, C, active=active, stream=side)
+            o_side = [x.clone() for x in o_side]
+        o_g, rep_g = graph.launch()
+        assert rep_side == rep_ref and rep_g == rep_ref, i
+        torch.cuda.current_stream().wait_stream(side)
+        for s in range(D):
+            assert torch.equal(o_side[s][0], o_ref[s][0]), (i, s)
+            assert torch.equal(o_g[s][0], o_ref[s][0]), (i, s)
+    torch.cuda.synchronize()
+    for r in (on_stream, graphed):
+        assert torch.equal(r.pool_k(), ref.pool_k()) and torch.equal(r.pool_v(), ref.pool_v())
+        assert r.view(1)["n_committed"] == 0
+    assert torch.count_nonzero(ref.pool_k()[1]) == 0   # the idle rollout's slots: still the zero fill
+    graph.close()
+    for r in (ref, on_stream, graphed):
+        r.close()
