@@ -165,3 +165,42 @@ def test_rope_tensor_size_limit_on_a_device_ring():
     assert L.wm_rope3d_pair(ring._h, p, p, 8, p, p, 256, 1, None, None, None) == 2
     torch.cuda.synchronize()
     ring.close()
+
+
+def test_reset_policy_refuses_whole_steps_before_any_launch():
+    """With WM_EVICT_RESET and the window full, wm_rollout_step and a graph
+    launch fail with WM_E_CAPACITY before anything is enqueued: outputs keep
+    their fill, bookkeeping and pool bytes are unchanged; after a reset both
+    run again."""
+    wl = Workload(320, "reset_step", 1, 4, 2, 128, 5, 6, 1, 1, 2, 0, 0, 2)
+    src = Source(wl)
+    B, C, D = 1, wl.chunk, wl.n_denoise
+    ring = wm.KVRing(B, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w, wl.n_sink,
+                     wl.window, C, evict_policy=wm.EVICT_RESET)
+    qs = [dev(src.batch_chunk([0], C, s, "q")) for s in range(D)]
+    ks = [dev(src.batch_chunk([0], C, s, "k")) for s in range(D)]
+    vs = [dev(src.batch_chunk([0], C, s, "v")) for s in range(D)]
+    outs = [torch.full_like(q, 5.0) for q in qs]
+    graph_outs = [torch.full_like(q, 5.0) for q in qs]
+    graph = ring.rollout_graph(qs, ks, vs, C, outs=graph_outs)
+    for _ in range(wl.n_sink + wl.window):        # fill sinks and window exactly
+        ring.rollout_step(qs, ks, vs, C)
+    torch.cuda.synchronize()
+    view, pool = ring.view(0), ring.pool.clone()
+    with pytest.raises(wm.WMError) as e1:
+        ring.rollout_step(qs, ks, vs, C, outs=outs)
+    with pytest.raises(wm.WMError) as e2:
+        graph.launch()
+    assert e1.value.name == "WM_E_CAPACITY" and e2.value.name == "WM_E_CAPACITY"
+    torch.cuda.synchronize()
+    assert ring.view(0) == view and torch.equal(ring.pool, pool)
+    five = torch.full_like(qs[0], 5.0)
+    assert all(torch.equal(o, five) for o in outs + graph_outs)
+    ring.reset(0, 0)
+    out_step, _ = ring.rollout_step(qs, ks, vs, C, outs=outs)
+    graph.launch()
+    torch.cuda.synchronize()
+    assert ring.view(0)["n_committed"] == 2
+    assert not any(torch.equal(o, five) for o in outs + graph_outs)
+    graph.close()
+    ring.close()
