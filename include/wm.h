@@ -236,7 +236,10 @@ wm_status wm_rope3d_pair(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, in
  * split count is chosen per launch from the workgroup count and key length;
  * the environment variable WM_ATTN_SPLIT=n (1..8) overrides it (tuning,
  * tests) and is also honoured by wm_chunk_attn_workspace_bytes().  A split
- * that does not fit the given workspace is reduced until it does.
+ * that does not fit the given workspace is reduced until it does.  The
+ * workspace (like the RoPE scratch of wm_rollout_step) is written and read by
+ * this call's launches on `stream`: calls that may run at the same time, on
+ * other streams, need workspaces of their own.
  * Errors: WM_E_ARG, WM_E_SHAPE, WM_E_STATE, WM_E_HIP. */
 wm_status wm_chunk_attn(const wm_kvring* ring, const wm_bf16* q_rot, const wm_bf16* k_rot,
                         const wm_bf16* v, int32_t n_frames, const uint8_t* active,

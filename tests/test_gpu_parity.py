@@ -429,6 +429,26 @@ def test_rope_pair_equals_two_single_launches(d, hq, hkv, views):
     ring.close()
 
 
+def test_rope_in_place_equals_out_of_place():
+    """y == x (and y2 == x2 for the pair) is allowed: each thread reads its
+    vectors before it writes them back, the exact second pass reads its
+    registers, so in place equals out of place bit for bit."""
+    wl = W(155, batch=2, n_q_heads=8, n_kv_heads=2, frame_h=5, frame_w=9, chunk=3)
+    ring, _ = make_ring(wl)
+    n = wl.chunk
+    q = full_range_bits(156, (2, n * wl.ft, 8, 128))
+    k = full_range_bits(157, (2, n * wl.ft, 2, 128))
+    want_q = host(ring.rope3d(dev(q), n))
+    want_k = host(ring.rope3d(dev(k), n))
+    xq, xk = dev(q), dev(k)
+    ring.rope3d(xq, n, y=xq)
+    assert np.array_equal(host(xq), want_q)
+    xq, xk = dev(q), dev(k)
+    ring.rope3d_pair(xq, xk, n, y=xq, y2=xk)
+    assert np.array_equal(host(xq), want_q) and np.array_equal(host(xk), want_k)
+    ring.close()
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads, steady state, sampled outputs
 # ---------------------------------------------------------------------------
