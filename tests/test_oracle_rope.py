@@ -74,19 +74,48 @@ def read_hand_examples():
         for line in fh:
             if line.startswith("#") or not line.strip():
                 continue
-            case, d, bands, pos, x, y = [c.strip() for c in line.split("|")]
+            cols = [c.strip() for c in line.split("|")]
+            case, d, bands, pos, x, y = cols[:6]
+            theta = float(cols[6]) if len(cols) > 6 else 10000.0
             out.append((case, int(d), tuple(int(v) for v in bands.split(",")),
                         tuple(int(v) for v in pos.split(",")),
-                        [float(v) for v in x.split(",")], [float(v) for v in y.split(",")]))
+                        [float(v) for v in x.split(",")], [float(v) for v in y.split(",")], theta))
     return out
 
 
 @pytest.mark.parametrize("ex", read_hand_examples(), ids=lambda e: e[0])
 def test_hand_examples(ex):
-    _, d, bands, (t, h, w), x, y = ex
+    _, d, bands, (t, h, w), x, y, theta = ex
     xb = bf16.f64_to_bits(np.array(x)).reshape(1, 1, d)
-    yb = rope.rotate(xb, np.array([t]), np.array([h]), np.array([w]), rope_dims=bands)
+    yb = rope.rotate(xb, np.array([t]), np.array([h]), np.array([w]), theta=theta, rope_dims=bands)
     assert list(bf16.bits_to_f64(yb).reshape(-1)) == y
+
+
+def test_rne_is_one_rounding_from_fp64():
+    """x just above a bf16 midpoint whose lower neighbour is even, closer to
+    it than half an fp32 spacing: rounded once from fp64 it goes up; rounded
+    to fp32 first it would land on the midpoint and tie down to even."""
+    for e in (-20, -3, 0, 1, 7, 60):
+        for k in (128, 130, 200, 254):                     # even 8-bit significands
+            q = 2.0 ** (e - 8)                              # bf16 spacing for |x| in [2^(e-1), 2^e)
+            x = (k + 0.5 + 2.0 ** -20) * q
+            up = bf16.bits_to_f64(bf16.f64_to_bits(np.array([x, -x])))
+            assert list(up) == [(k + 1) * q, -(k + 1) * q], (e, k)
+            x = (k + 0.5 - 2.0 ** -20) * q
+            assert bf16.bits_to_f64(bf16.f64_to_bits(np.array([x])))[0] == k * q, (e, k)
+
+
+def test_tables_hold_fp32_values():
+    """The (cos, sin) tables are libm fp64 values rounded once to fp32: every
+    entry is an fp32 number, and it is the fp32 number nearest to libm's."""
+    for pos in (0, 1, 7, 1234, 99991):
+        for d_a in (2, 20, 44):
+            c, s_ = rope.table_row(pos, 10000.0, d_a)
+            assert np.array_equal(c.astype(np.float32).astype(np.float64), c)
+            assert np.array_equal(s_.astype(np.float32).astype(np.float64), s_)
+            j = d_a // 2 - 1
+            ang = pos * math.pow(10000.0, -(2.0 * j) / d_a)
+            assert c[j] == float(np.float32(math.cos(ang))) and s_[j] == float(np.float32(math.sin(ang)))
 
 
 def test_default_band_split():
