@@ -135,6 +135,45 @@ def _commit_unrotated(self, k_raw_bits, v_bits, n_frames):
     return written, evicted
 
 
+def _bits_to_f64_shift15(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+    return b.view(np.float32).astype(np.float64)
+
+
+def _attend_masked_inverted(q, k, v, mask, scale=None, heads=None):
+    return _ATTEND_MASKED(q, k, v, ~np.asarray(mask), scale, heads)
+
+
+_ATTEND_MASKED = attention.attend_masked
+
+
+def _frame_visible_window_long(f, n0, n_frames, n_sink, window):
+    in_chunk = n0 <= f < n0 + n_frames
+    is_sink = f < n_sink and f < n0 + n_frames
+    in_window = window > 0 and max(n_sink, n0 - window - 1) <= f < n0
+    return in_chunk or is_sink or in_window
+
+
+def _t_of_plus_one(self, frame):
+    return self.t0 + frame + 1
+
+
+def _keys_values_own_chunk_first(self, k_rot_chunk, v_chunk, n_frames):
+    n0 = self.n_committed
+    frames = attention.visible_frames(n0, n_frames, self.S, self.W)
+    ks, vs = [], []
+    for f in frames:
+        if f >= n0:
+            continue
+        kb, vb = self.cache[f]
+        ks.append(kb)
+        vs.append(vb)
+    # the chunk's keys paired with the values of the frame before them
+    ks.append(k_rot_chunk)
+    vs.append(np.roll(np.asarray(v_chunk), self.ft, axis=0))
+    return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
+
+
 def _f64_to_bits(mode):
     def f64_to_bits(x):
         x = np.asarray(x, dtype=np.float64)
@@ -238,6 +277,11 @@ MUTATIONS = {
     "visible keys: sinks before they exist": (ATT + RING, [(attention, "visible_frames", _visible_frames(early_sinks=True)),
                                                           (pins_ring, "visible_frames", _visible_frames(early_sinks=True))]),
     "commit: K stored unrotated": (ATT, [(Rollout, "commit", _commit_unrotated)]),
+    "bf16: decoded with the wrong shift": (ROPE, [(bf16, "bits_to_f64", _bits_to_f64_shift15)]),
+    "masked formulation: mask inverted": (ATT, [(attention, "attend_masked", _attend_masked_inverted)]),
+    "masked formulation: window one frame long": (ATT, [(attention, "frame_visible", _frame_visible_window_long)]),
+    "rollout: positions one frame late": (ATT, [(Rollout, "t_of", _t_of_plus_one)]),
+    "rollout: chunk values shifted by a frame": (ATT, [(Rollout, "keys_values", _keys_values_own_chunk_first)]),
     "ring: evicts the newest frame": (RING, [(ring.DequeRing, "commit", _commit(evict_newest=True))]),
     "ring: highest free slot first": (RING, [(ring.DequeRing, "commit", _commit(highest_free=True))]),
     "ring: sinks evicted like window frames": (RING, [(ring.DequeRing, "commit", _commit(evict_sinks=True))]),
