@@ -229,6 +229,9 @@ wm_status wm_rope3d_pair(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, in
  * v     : bf16 [B][n_frames*Ft][Hkv][d]
  * out   : bf16 [B][n_frames*Ft][Hq][d], round-to-nearest-even of the fp32
  *         result (bf16 MFMA products, fp32 accumulation and softmax).
+ * Inputs must be finite and every scaled score q.k*scale finite in fp32;
+ * NaN or infinite inputs, or scores that overflow fp32, are outside the
+ * contract (the kernel does not screen for them).
  * softmax_scale <= 0 selects 1/sqrt(d).
  * workspace: optional device scratch for splitting long key ranges across
  * workgroups (more parallelism when B*Hq*Nq is small); NULL/0 = no split.
