@@ -88,7 +88,7 @@ typedef enum {
   WM_E_STATE = 3,       /* destroyed handle, metadata-only ring, bad state */
   WM_E_CAPACITY = 4,    /* pool or workspace too small                     */
   WM_E_HIP = 5,         /* a HIP call failed                               */
-  WM_E_UNSUPPORTED = 6  /* valid request this build does not implement     */
+  WM_E_UNSUPPORTED = 6  /* valid request the library does not implement    */
 } wm_status;
 
 typedef struct {
