@@ -2,7 +2,8 @@
 //
 // What it computes (Cosmos3-H-Dreams model card, "Model Architecture":
 // block-causal student with a KV cache; AlpaDreams GTC write-up, section VII:
-// next frame from historical clean frames + the current noisy frame): for
+// a new frame is predicted from the denoised earlier frames and the noisy
+// current one): for
 // each query of the current chunk, softmax attention over the keys of the
 // frames the rollout holds (sinks + window, from the ring pool) and of every
 // frame of the chunk itself.  The visible ring slots of a rollout that has

@@ -14,14 +14,16 @@
  * Sources (web pages; section names given):
  *  - FlashDreams blog post ("NVIDIA FlashDreams Is the Open-Source Inference
  *    Engine Robotics World Models Needed"), "Bounded Memory for Infinite
- *    Rollouts": a per-rollout cache with bounded VRAM and internal eviction;
+ *    Rollouts": every rollout owns a cache of fixed device memory and drops
+ *    old entries by itself;
  *    "Hot-Path Generation, Background State Updates": each step splits into
  *    generate() (denoising) and finalize() (KV-cache update).
  *  - Cosmos3-H-Dreams model card, "Model Architecture": block-causal few-step
  *    student with a KV cache; the conditioning frame is prefilled once;
  *    "Software Integration": static-shape KV cache, BF16.
- *  - AlpaDreams GTC write-up, section VII: the causal DiT produces the next
- *    frame from the historical clean frames and the current noisy frame.
+ *  - AlpaDreams GTC write-up, section VII: the causal DiT predicts each new
+ *    frame from the earlier, already denoised frames together with the frame
+ *    still being denoised.
  *  - DreamZero single-GPU page, "Sequential requests": frame positions and the
  *    cache persist across requests; explicit start frame / cache reset.
  *

@@ -19,9 +19,9 @@ computes, written from the source pages:
                    temporal order, plus the equivalent masked full-sequence
                    formulation (Cosmos3-H-Dreams model card, "Model
                    Architecture": block-causal student with a KV cache;
-                   AlpaDreams write-up, section VII: the causal DiT produces the
-                   next frame from historical clean frames and the current
-                   noisy frame).
+                   AlpaDreams write-up, section VII: each new frame is
+                   predicted from the earlier, already denoised frames and
+                   the frame still being denoised).
 * ``rollout``   -- a whole rollout: prefill, chunks of few-step denoising,
                    commit after the last step (FlashDreams blog post,
                    "Hot-Path Generation, Background State Updates").

@@ -3,8 +3,8 @@
 Pages:
 * Cosmos3-H-Dreams model card, "Model Architecture": the few-step student is
   block-causal and generates autoregressively with a KV cache.
-* AlpaDreams write-up, section VII: the causal DiT generates the next frame
-  from historical clean frames plus the current noisy frame.
+* AlpaDreams write-up, section VII: the causal DiT predicts each new frame
+  from the earlier, already denoised frames and the frame being denoised.
 * FlashDreams blog post, "Bounded Memory for Infinite Rollouts": the cache a
   chunk attends to is bounded.
 

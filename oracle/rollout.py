@@ -2,8 +2,9 @@
 
 Pages:
 * FlashDreams blog post, "Hot-Path Generation, Background State Updates":
-  each autoregressive step is a latency-critical generate() (few-step
-  denoising) followed by finalize() (KV-cache update and state upkeep).
+  a rollout step splits into generate(), the few-step denoising whose
+  latency counts, and finalize(), which brings the KV cache and the rest of
+  the state up to date.
 * Cosmos3-H-Dreams model card, "Model Architecture": the conditioning frame is
   prefilled into the KV cache once; then each latent frame takes 4 denoising
   steps.  The Cosmos-H-Dreams news item and the AlpaDreams write-up (section
