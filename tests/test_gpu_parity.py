@@ -429,6 +429,39 @@ def test_rope_pair_equals_two_single_launches(d, hq, hkv, views):
     ring.close()
 
 
+def test_large_frame_sampled():
+    """A 512 x 512-token frame (262,144 tokens; 786,432 visible keys): the
+    token -> (slot, row) and (h, w) arithmetic at large indices.  RoPE is
+    bit-exact on the whole chunk, attention matches the oracle on sampled
+    rows, and the appended frame's pool bytes are exact."""
+    wl = W(141, n_q_heads=2, n_kv_heads=1, head_dim=64, frame_h=512, frame_w=512, chunk=1, n_sink=1,
+           window=1, n_gen=3)
+    src = Source(wl)
+    ring, oracles = make_ring(wl)
+    ro = oracles[0]
+    for n0 in range(2):   # fill sink and window
+        k_np, v_np = src.batch_chunk([n0], 1, -1, "k"), src.batch_chunk([n0], 1, -1, "v")
+        ring.append_evict(dev(k_np), dev(v_np), 1)
+        ro.commit(k_np[0], v_np[0], 1)
+    q_np, k_np, v_np = (src.batch_chunk([2], 1, 0, x) for x in "qkv")
+    q_rot, k_rot = ring.rope3d_pair(dev(q_np), dev(k_np), 1)
+    out = host(ring.chunk_attn(q_rot, k_rot, dev(v_np), 1, workspace=workspace_for(ring, 1)))
+    ref_q, ref_k = ro.rope(q_np[0], 1), ro.rope(k_np[0], 1)
+    assert np.array_equal(host(q_rot)[0], ref_q) and np.array_equal(host(k_rot)[0], ref_k)
+    nq = wl.ft
+    rng = np.random.default_rng(141)
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(nq - 64, nq), rng.integers(0, nq, 192)]))
+    ref = ro.attend(ref_q, ref_k, v_np[0], 1, rows=rows)
+    for h in range(2):
+        assert_close(out[0][rows][:, h], ref[:, h], "large frame head %d" % h)
+    rep = ring.append_evict(dev(k_np), dev(v_np), 1)
+    written, evicted = ro.commit(k_np[0], v_np[0], 1)
+    assert rep[0] == {"written": written, "evicted": evicted}
+    f, slot, _ = ro.retained()[-1]
+    assert np.array_equal(host(ring.pool_k())[0, slot], ro.cache[f][0].transpose(1, 0, 2))
+    ring.close()
+
+
 def test_rope_in_place_equals_out_of_place():
     """y == x (and y2 == x2 for the pair) is allowed: each thread reads its
     vectors before it writes them back, the exact second pass reads its
