@@ -397,6 +397,28 @@ def test_rope_explicit_t_first_and_inactive_rows_untouched():
     ring.close()
 
 
+def test_rope_at_very_large_positions():
+    """t up to the 2^52 limit: the t-band tables of the library (host libm)
+    and of the oracle agree, and so do the rotated bits; the append commits
+    at such positions after a reset."""
+    wl = W(122, batch=3, frame_h=3, frame_w=5, chunk=2)
+    ring, oracles = make_ring(wl, t0s=[(1 << 40) + 3, (1 << 52) - 7, 987654321987])
+    src = Source(wl)
+    x = src.batch_chunk([0, 0, 0], 2, 0, "q")
+    got = host(ring.rope3d(dev(x), 2))
+    for b in range(3):
+        assert np.array_equal(got[b], oracles[b].rope(x[b], 2)), b
+    k, v = src.batch_chunk([0, 0, 0], 2, -1, "k"), src.batch_chunk([0, 0, 0], 2, -1, "v")
+    reps = ring.append_evict(dev(k), dev(v), 2)
+    pk = host(ring.pool_k())
+    for b in range(3):
+        written, evicted = oracles[b].commit(k[b], v[b], 2)
+        assert reps[b] == {"written": written, "evicted": evicted}
+        for f, slot, t in oracles[b].retained():
+            assert np.array_equal(pk[b, slot], oracles[b].cache[f][0].transpose(1, 0, 2)), (b, f)
+    ring.close()
+
+
 @pytest.mark.parametrize("d,hq,hkv,views", [(128, 6, 3, 1), (64, 9, 3, 2)])
 def test_rope_pair_equals_two_single_launches(d, hq, hkv, views):
     """wm_rope3d_pair (Q and K in one launch; head counts that leave a partial
