@@ -397,6 +397,39 @@ def test_rope_explicit_t_first_and_inactive_rows_untouched():
     ring.close()
 
 
+@pytest.mark.parametrize("d,theta,dims", [(128, 500000.0, (64, 32, 32)), (64, 16.0, (8, 28, 28))])
+def test_custom_theta_and_bands(d, theta, dims):
+    """A non-default RoPE base and band split (the t band at its 64-wide
+    maximum in the first case): RoPE of Q and K bit-exact, attention within
+    tolerance and pool bytes exact over a short rollout through the step."""
+    B, hq, hkv, fh, fw, S, Wn, C = 2, 4, 2, 5, 7, 1, 2, 2
+    ring = wm.KVRing(B, hq, hkv, d, fh, fw, S, Wn, C, rope_theta=theta, rope_dims=dims)
+    oracles = [Rollout(hq, hkv, d, fh, fw, S, Wn, theta=theta, rope_dims=dims) for _ in range(B)]
+    wl = W(150 + d, batch=B, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, frame_h=fh, frame_w=fw, chunk=C,
+           n_sink=S, window=Wn, n_gen=8, n_denoise=2)
+    src = Source(wl)
+    for ci in range(4):
+        n0 = ci * C
+        qs = [src.batch_chunk([n0] * B, C, s, "q") for s in range(2)]
+        ks = [src.batch_chunk([n0] * B, C, s, "k") for s in range(2)]
+        vs = [src.batch_chunk([n0] * B, C, s, "v") for s in range(2)]
+        q_rot, k_rot = ring.rope3d_pair(dev(qs[0]), dev(ks[0]), C)
+        outs, reps = ring.rollout_step([dev(x) for x in qs], [dev(x) for x in ks], [dev(x) for x in vs], C)
+        for b in range(B):
+            rq, rk = oracles[b].rope(qs[0][b], C), oracles[b].rope(ks[0][b], C)
+            assert np.array_equal(host(q_rot)[b], rq) and np.array_equal(host(k_rot)[b], rk), (ci, b)
+            for s_ in range(2):
+                _, _, ref = oracles[b].denoise_step(qs[s_][b], ks[s_][b], vs[s_][b], C)
+                assert_close(host(outs[s_])[b], ref, "theta %g chunk %d b %d s %d" % (theta, ci, b, s_))
+            written, evicted = oracles[b].commit(ks[-1][b], vs[-1][b], C)
+            assert reps[b] == {"written": written, "evicted": evicted}
+    pk = host(ring.pool_k())
+    for b in range(B):
+        for f, slot, t in oracles[b].retained():
+            assert np.array_equal(pk[b, slot], oracles[b].cache[f][0].transpose(1, 0, 2)), (b, f)
+    ring.close()
+
+
 def test_rope_at_very_large_positions():
     """t up to the 2^52 limit: the t-band tables of the library (host libm)
     and of the oracle agree, and so do the rotated bits; the append commits
