@@ -430,6 +430,29 @@ def test_custom_theta_and_bands(d, theta, dims):
     ring.close()
 
 
+@pytest.mark.parametrize("scale", [0.03, 0.25, 1.0, 0.0])
+def test_explicit_softmax_scale(scale):
+    """wm_chunk_attn with an explicit scale (0 selects 1/sqrt(d)) against the
+    oracle with the same scale; a NaN scale is refused."""
+    wl = W(160, n_q_heads=4, n_kv_heads=2, frame_h=6, frame_w=9, chunk=2, window=3, n_gen=4)
+    src = Source(wl)
+    ring, oracles = make_ring(wl)
+    ro = oracles[0]
+    for n0 in range(4):
+        k_np, v_np = src.batch_chunk([n0], 1, -1, "k"), src.batch_chunk([n0], 1, -1, "v")
+        ring.append_evict(dev(k_np), dev(v_np), 1)
+        ro.commit(k_np[0], v_np[0], 1)
+    q_np, k_np, v_np = (src.batch_chunk([4], 2, 0, x) for x in "qkv")
+    q_rot, k_rot = ring.rope3d_pair(dev(q_np), dev(k_np), 2)
+    out = host(ring.chunk_attn(q_rot, k_rot, dev(v_np), 2, scale=scale))
+    ref = ro.attend(host(q_rot)[0], host(k_rot)[0], v_np[0], 2, scale=scale if scale > 0 else None)
+    assert_close(out[0], ref, "scale %g" % scale)
+    with pytest.raises(wm.WMError) as e:
+        ring.chunk_attn(q_rot, k_rot, dev(v_np), 2, scale=float("nan"))
+    assert e.value.name == "WM_E_ARG"
+    ring.close()
+
+
 def test_rope_at_very_large_positions():
     """t up to the 2^52 limit: the t-band tables of the library (host libm)
     and of the oracle agree, and so do the rotated bits; the append commits
