@@ -158,6 +158,33 @@ def cpu_baseline(wl, n_heads):
             "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model, "blas": blas}
 
 
+def cpu_baseline_others():
+    """The oracle on one steady-state denoise step (all heads) of the drive and
+    32/8-head GQA workloads, and on the whole tiny rollout."""
+    from oracle.rollout import Rollout
+    from wm_synth import WORKLOADS, Source
+    out = []
+    for wid in (3, 4):
+        r = cpu_baseline(WORKLOADS[wid], WORKLOADS[wid].n_q_heads)
+        out.append({"workload": WORKLOADS[wid].name, "value": r["value"], "unit": r["unit"], "sample": r["sample"]})
+    wl = WORKLOADS[1]
+    src = Source(wl)
+    ro = Rollout(wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w, wl.n_sink, wl.window)
+    t0 = time.perf_counter()
+    flops = 0.0
+    for c in wl.chunks():
+        n0 = ro.n_committed
+        for s in range(wl.n_denoise):
+            ro.denoise_step(src.chunk(0, n0, c, s, "q"), src.chunk(0, n0, c, s, "k"), src.chunk(0, n0, c, s, "v"), c)
+            flops += wl.attn_flops(n_q=c * wl.ft, n_k=(min(n0, wl.n_sink + wl.window) + c) * wl.ft)
+        ro.commit(src.chunk(0, n0, c, wl.n_denoise - 1, "k"), src.chunk(0, n0, c, wl.n_denoise - 1, "v"), c)
+    dt = time.perf_counter() - t0
+    out.append({"workload": wl.name, "value": flops / dt / 1e12, "unit": "TFLOP/s",
+                "sample": "the whole %d-frame rollout (%d denoise steps per chunk), fp64 NumPy; %.2f s"
+                          % (wl.n_gen, wl.n_denoise, dt)})
+    return out
+
+
 def whole_rollout(torch, wm, wl, dev, qs, ks, vs, outs, q_rot, k_rot, heat, reps=3):
     """A whole rollout from an empty ring (prefill, then every chunk, the
     window filling on the way): algorithmic attention flops of all steps /
@@ -555,6 +582,8 @@ def main():
     ring.close()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)
+        if not args.steady_only:
+            result["cpu_baseline"]["other_workloads"] = cpu_baseline_others()
     try:
         result["git"] = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short", "HEAD"],
                                        capture_output=True, text=True).stdout.strip() or None
