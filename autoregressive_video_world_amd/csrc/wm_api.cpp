@@ -697,7 +697,10 @@ wm_status plan_graph_step(wm_rollout_graph* g, std::vector<PLaunch>* plan, wm_ap
 }
 
 // A graph of the planned launches in one dependency chain, and its instance.
+// A step with no active rollout plans no launch: then there is no graph and
+// a launch enqueues only the completion event.
 hipError_t build_graph(wm_rollout_graph* g, std::vector<PLaunch>& plan) {
+  if (plan.empty()) return hipSuccess;
   hipError_t e = hipGraphCreate(&g->graph, 0);
   for (size_t i = 0; e == hipSuccess && i < plan.size(); ++i) {
     hipKernelNodeParams kp = node_params(plan[i]);
@@ -1074,7 +1077,7 @@ wm_status wm_rollout_graph_launch(wm_rollout_graph* g, wm_append_report* rep, in
     e = build_graph(g, plan);
     if (e != hipSuccess) drop_graph(g);
   }
-  if (e == hipSuccess) e = hipGraphLaunch(g->exec, s);
+  if (e == hipSuccess && g->exec) e = hipGraphLaunch(g->exec, s);
   if (e == hipSuccess) e = hipEventRecord(g->ev_done, s);
   if (e != hipSuccess) return hip_fail(e, "graph launch");
   g->launched = true;

@@ -37,6 +37,8 @@
  *    frame*Ft + view*frame_h*frame_w + h*frame_w + w (Ft = views * frame_h *
  *    frame_w; one view unless the descriptor says more), B = desc.batch (every
  *    rollout has a row block, active or not).
+ *  - `active` (host [B] or NULL = all): a call whose mask names no rollout
+ *    is valid and enqueues nothing.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every launch of a
  *    call goes onto that stream; no call synchronizes the device or copies
  *    device data to the host, with two exceptions: wm_kvring_create (a
@@ -337,7 +339,8 @@ wm_status wm_rollout_step(wm_kvring* ring, int32_t n_denoise, const wm_bf16* con
  * wm_rollout_graph_create builds a graph of the launches wm_rollout_step
  * would make for these buffers (fixed for the graph's life) and this active
  * set, from the ring as it is now; it changes nothing.  The graph holds only
- * kernel nodes, in one dependency chain.
+ * kernel nodes, in one dependency chain (none when no rollout is active: a
+ * launch then runs nothing).
  * wm_rollout_graph_launch runs one step: it plans the step from the ring's
  * bookkeeping (positions, slots, visible frames), writes those parameters
  * into the graph's nodes and launches the graph on `stream`, then commits

@@ -203,6 +203,20 @@ def test_zero_window_stores_sinks_only():
     r.close()
 
 
+def test_append_with_no_active_rollout_changes_nothing():
+    r = wm.KVRing(3, 2, 2, 64, 2, 2, 1, 2, 2, meta_only=True)
+    r.append_evict(None, None, 2)
+    views = [r.view(b) for b in range(3)]
+    for _ in range(4):
+        assert r.append_evict(None, None, 2, active=[0, 0, 0]) == [{"written": [], "evicted": []}] * 3
+    assert [r.view(b) for b in range(3)] == views
+    dq = DequeRing(1, 2)
+    oracle_append(dq, 2, 0)
+    assert r.append_evict(None, None, 2, active=[0, 1, 0])[1] == oracle_append(dq, 2, 0)
+    assert r.view(0) == views[0] and r.view(2) == views[2]
+    r.close()
+
+
 # ---------------------------------------------------------------------------
 # validation and error codes (no HIP call is reached)
 # ---------------------------------------------------------------------------

@@ -276,3 +276,63 @@ def test_created_stream_and_graph_with_active_mask():
     graph.close()
     for r in (ref, on_stream, graphed):
         r.close()
+
+
+def test_steps_with_no_active_rollout_change_nothing():
+    """Calls whose active mask names no rollout enqueue nothing: RoPE and
+    attention outputs keep their fill, every report is empty, pools and
+    bookkeeping are unchanged (eager, finalize stream, and a graph, which
+    then has no kernel node); the next active step matches a ring that never
+    saw those calls."""
+    wl = CASES["gqa_batch2"]
+    B, C, D = wl.batch, wl.chunk, wl.n_denoise
+    src = Source(wl)
+    ring, ref = new_ring(wl), new_ring(wl)
+    qs = [dev(src.batch_chunk([0] * B, C, s, "q")) for s in range(D)]
+    ks = [dev(src.batch_chunk([0] * B, C, s, "k")) for s in range(D)]
+    vs = [dev(src.batch_chunk([0] * B, C, s, "v")) for s in range(D)]
+    for r in (ring, ref):
+        r.rollout_step(qs, ks, vs, C)
+    torch.cuda.synchronize()
+    none = [0] * B
+    pool_k, pool_v = ring.pool_k().clone(), ring.pool_v().clone()
+    views = [ring.view(b) for b in range(B)]
+    fill = torch.full_like(qs[0], 7.0)
+    empty = [{"written": [], "evicted": []}] * B
+
+    y = ring.rope3d(qs[0], C, y=fill.clone(), active=none)
+    y2, y3 = ring.rope3d_pair(qs[0], ks[0], C, y=fill.clone(), y2=torch.full_like(ks[0], 7.0), active=none)
+    o = ring.chunk_attn(qs[0], ks[0], vs[0], C, out=fill.clone(), active=none)
+    assert torch.equal(y, fill) and torch.equal(y2, fill) and torch.equal(o, fill)
+    assert torch.count_nonzero(y3 != 7.0) == 0
+    assert ring.append_evict(ks[-1], vs[-1], C, active=none) == empty
+    outs = [fill.clone() for _ in range(D)]
+    _, reps = ring.rollout_step(qs, ks, vs, C, outs=outs, active=none)
+    assert reps == empty and all(torch.equal(x, fill) for x in outs)
+    fin = torch.cuda.Stream()
+    _, reps = ring.rollout_step(qs, ks, vs, C, outs=outs, active=none, finalize_stream=fin)
+    assert reps == empty
+    g_outs = [fill.clone() for _ in range(D)]
+    graph = ring.rollout_graph(qs, ks, vs, C, outs=g_outs, active=none)
+    for _ in range(3):
+        _, reps = graph.launch()
+        assert reps == empty
+        torch.cuda.synchronize()
+    graph.close()
+    torch.cuda.current_stream().wait_stream(fin)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, fill) for x in outs + g_outs)
+    assert torch.equal(ring.pool_k(), pool_k) and torch.equal(ring.pool_v(), pool_v)
+    assert [ring.view(b) for b in range(B)] == views
+
+    qs2 = [dev(src.batch_chunk([C] * B, C, s, "q")) for s in range(D)]
+    ks2 = [dev(src.batch_chunk([C] * B, C, s, "k")) for s in range(D)]
+    vs2 = [dev(src.batch_chunk([C] * B, C, s, "v")) for s in range(D)]
+    o_a, rep_a = ring.rollout_step(qs2, ks2, vs2, C)
+    o_b, rep_b = ref.rollout_step(qs2, ks2, vs2, C)
+    torch.cuda.synchronize()
+    assert rep_a == rep_b
+    assert all(torch.equal(a, b) for a, b in zip(o_a, o_b))
+    assert torch.equal(ring.pool_k(), ref.pool_k()) and torch.equal(ring.pool_v(), ref.pool_v())
+    ring.close()
+    ref.close()
