@@ -35,9 +35,27 @@ def errors(got_bits, ref):
     return float(d.max()), float(d.mean()), rel
 
 
-def assert_close(got_bits, ref, what=""):
+# Inputs outside the N(0,1) workloads (queries scaled x8: a peaked softmax
+# with |O| up to max|V| ~ 5) meet the arithmetic's own limit first.  P is
+# rounded to bf16 before P.V and O is written in bf16, each with unit
+# roundoff u = 2^-8, so even an exact fp32 pipeline is off by up to
+# u * (sum_k p_k |v_k| / l) + u * |O| <= u * (max|V| + |O|): ~0.03 at
+# |O| = 4, where bf16 values are 2^-5 apart.  For such inputs an element may
+# use that bound (plus 1e-3 for the fp32 sums and exponentials) where it is
+# above MAX_ABS; the mean-abs and relative-L2 gates stay as they are.
+BF16_U = 2.0 ** -8
+
+
+def assert_close(got_bits, ref, what="", vmax=None):
+    """The acceptance bar; with vmax (max |V| of the case's inputs), the
+    per-element bound is max(MAX_ABS, u * (|ref| + vmax) + 1e-3)."""
     mx, mean, rel = errors(got_bits, ref)
     assert np.all(np.isfinite(bf16_to_f64(got_bits))), what
-    assert mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_L2, \
+    if vmax is None:
+        ok_elem = mx <= MAX_ABS
+    else:
+        bound = np.maximum(MAX_ABS, BF16_U * (np.abs(ref) + vmax) + 1e-3)
+        ok_elem = bool(np.all(np.abs(bf16_to_f64(got_bits) - ref) <= bound))
+    assert ok_elem and mean <= MEAN_ABS and rel <= REL_L2, \
         "%s: max %.3g mean %.3g relL2 %.3g" % (what, mx, mean, rel)
     return mx, mean, rel

@@ -21,7 +21,7 @@ from oracle.rollout import Rollout
 from oracle import bf16 as obf16
 from oracle import rope as orope
 from wm_synth import Source, Workload, WORKLOADS, full_range_bits
-from gpu_util import assert_close, dev, host
+from gpu_util import assert_close, bf16_to_f64, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -101,6 +101,8 @@ def _run_case(wl, t0s, use_step, q_scale, split):
     used = [set() for _ in range(B)]
     n_steps = max(wl.stagger * b + len(actions[b]) for b in range(B))
     worst = [0.0, 0.0, 0.0]
+    # N(0,1) queries: the stated bar; scaled queries: the bf16 bound as well
+    vmax = 0.0 if q_scale != 1.0 else None
     for g in range(n_steps):
         groups = {}
         for b in range(B):
@@ -113,12 +115,16 @@ def _run_case(wl, t0s, use_step, q_scale, split):
             if kind == "prefill":
                 k_np = src.batch_chunk(n0s, n, -1, "k")
                 v_np = src.batch_chunk(n0s, n, -1, "v")
+                if vmax is not None:
+                    vmax = max(vmax, float(np.abs(bf16_to_f64(v_np)).max()))
             else:
                 qs, ks, vs, outs_ref = [], [], [], []
                 for s in range(wl.n_denoise):
                     q_np = src.batch_chunk(n0s, n, s, "q")
                     k_np = src.batch_chunk(n0s, n, s, "k")
                     v_np = src.batch_chunk(n0s, n, s, "v")
+                    if vmax is not None:
+                        vmax = max(vmax, float(np.abs(bf16_to_f64(v_np)).max()))
                     qs.append(q_np)
                     ks.append(k_np)
                     vs.append(v_np)
@@ -132,7 +138,8 @@ def _run_case(wl, t0s, use_step, q_scale, split):
                     for s in range(wl.n_denoise):
                         got = host(outs[s])
                         for b in bs:
-                            errs = assert_close(got[b], outs_ref[s][b][2], "step %d b %d s %d" % (g, b, s))
+                            errs = assert_close(got[b], outs_ref[s][b][2], "step %d b %d s %d" % (g, b, s),
+                                                vmax)
                             worst = [max(a, e) for a, e in zip(worst, errs)]
                 else:
                     for s in range(wl.n_denoise):
@@ -145,7 +152,7 @@ def _run_case(wl, t0s, use_step, q_scale, split):
                             ref_q, ref_k, ref_o = outs_ref[s][b]
                             assert np.array_equal(qr[b], ref_q), ("q_rot", g, b, s)
                             assert np.array_equal(kr[b], ref_k), ("k_rot", g, b, s)
-                            errs = assert_close(o[b], ref_o, "step %d b %d s %d" % (g, b, s))
+                            errs = assert_close(o[b], ref_o, "step %d b %d s %d" % (g, b, s), vmax)
                             worst = [max(a, e) for a, e in zip(worst, errs)]
                 k_np, v_np = ks[-1], vs[-1]
             if kind == "prefill" or not use_step:
@@ -272,6 +279,19 @@ def test_rollout_parity_sharp_queries(name):
     row maxima that jump across key tiles, so the running-max rescale runs."""
     run_case(CASES[name], q_scale=8.0)
     run_case(CASES[name], q_scale=8.0, split=True)
+
+
+# Seeded sweep cases with queries scaled x8, among them two whose outputs
+# reach |O| ~ 4.2, where the bf16 bound is above the flat 2e-2 (errors of
+# 0.020 and 0.022 there, 1.3 u |O|).
+SHARP_SWEEP = [c for i, c in enumerate(sweep_cases(n=300, seed=31337)) if i in (89, 128) or i % 25 == 2]
+
+
+@pytest.mark.parametrize("i", range(len(SHARP_SWEEP)))
+def test_rollout_parity_sweep_sharp_queries(i):
+    wl, use_step, split = SHARP_SWEEP[i]
+    print("sharp sweep", i, wl, "use_step", use_step, "split", split, flush=True)
+    run_case(wl, use_step=use_step, split=split, q_scale=8.0)
 
 
 def test_rollout_parity_absolute_origins():
