@@ -38,7 +38,7 @@
  *    frame_w; one view unless the descriptor says more), B = desc.batch (every
  *    rollout has a row block, active or not).
  *  - `active` (host [B] or NULL = all): a call whose mask names no rollout
- *    is valid and enqueues nothing.
+ *    is valid and launches no kernel (stream-ordering events aside).
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every launch of a
  *    call goes onto that stream; no call synchronizes the device or copies
  *    device data to the host, with two exceptions: wm_kvring_create (a
