@@ -21,3 +21,20 @@ def test_readme_example_runs(capsys):
     assert printed[0] == "{'written': [(0, 0, 0), (1, 1, 1), (2, 2, 2)], 'evicted': []}"
     assert printed[1] == "{'retained': [(0, 0, 0), (1, 1, 1), (2, 2, 2)], 'n_committed': 3, 't0': 0}"
     assert len(scope["outs"]) == scope["D"]
+
+
+def test_readme_example_names_exist():
+    """On the CPU: every ring method and package name the example uses is
+    part of the binding."""
+    import autoregressive_video_world_amd as wm
+
+    src = open(os.path.join(ROOT, "README.md")).read()
+    code = re.findall(r"```python\n(.*?)```", src, re.S)[0]
+    compile(code, "README.md example", "exec")
+    methods = set(re.findall(r"\bring\.(\w+)\(", code))
+    assert methods and all(hasattr(wm.KVRing, m) for m in methods), methods
+    names = set(re.findall(r"\bwm\.(\w+)", code))
+    assert all(hasattr(wm, n) for n in names), names
+    # the lower-level calls the text names
+    for m in ("rope3d", "rope3d_pair", "chunk_attn", "append_evict", "rollout_graph"):
+        assert "`%s`" % m in src and hasattr(wm.KVRing, m), m
