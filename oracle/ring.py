@@ -69,9 +69,3 @@ class DequeRing:
 
     def retained_frames(self):
         return [f for f, _ in self.retained()]
-
-    def slot_of(self, frame):
-        for f, s in self.retained():
-            if f == frame:
-                return s
-        raise KeyError(frame)

@@ -221,3 +221,48 @@ def test_shift_of_all_positions_changes_little():
     _, r1, _, _ = run_rollout(1, 2, 1, 0, 4, 1, seed=3, t0=37)
     for a, b in zip(r0, r1):
         assert np.max(np.abs(a[5] - b[5])) < 5e-2
+
+
+def test_reset_starts_a_fresh_sequence_at_new_origin():
+    """DreamZero page, "Sequential requests": a new request resets the cache
+    and the start frame.  After a reset to origin t0, the rollout is the one a
+    new rollout at t0 produces from the same inputs (RoPE bits, keys, O bit
+    for bit); its outputs equal block-causal attention over the post-reset
+    frames alone; committed frames carry t = t0 + frame; and the cache holds
+    exactly the retained frames (nothing of the old sequence)."""
+    S, W, C, D = 1, 2, 1, 2
+    Hq = Hkv = 2
+    d, fh, fw = 32, 2, 3
+    ft = fh * fw
+    rng = np.random.default_rng(41)
+
+    def draw(n, H):
+        return to_bf16_bits(rng.standard_normal((n * ft, H, d)).astype(np.float32))
+
+    used = Rollout(Hq, Hkv, d, fh, fw, S, W, t0=5)
+    for _ in range(6):                    # an old sequence, past eviction
+        used.denoise_step(draw(1, Hq), draw(1, Hkv), draw(1, Hkv), 1)
+        used.commit(draw(1, Hkv), draw(1, Hkv), 1)
+    t0 = 1000
+    used.reset(t0)
+    fresh = Rollout(Hq, Hkv, d, fh, fw, S, W, t0=t0)
+    assert used.n_committed == 0 and used.retained() == [] and used.cache == {}
+    committed_k, committed_v = {}, {}
+    for n0 in range(4):                   # sink + window fill + first eviction
+        step_in = [(draw(C, Hq), draw(C, Hkv), draw(C, Hkv)) for _ in range(D)]
+        for q, k, v in step_in:
+            qa, ka, oa = used.denoise_step(q, k, v, C)
+            qb, kb, ob = fresh.denoise_step(q, k, v, C)
+            assert np.array_equal(qa, qb) and np.array_equal(ka, kb)
+            assert np.array_equal(oa, ob)
+            ks_a, vs_a = used.keys_values(ka, v, C)
+            ks_b, vs_b = fresh.keys_values(kb, v, C)
+            assert np.array_equal(ks_a, ks_b) and np.array_equal(vs_a, vs_b)
+            # block-causal attention over the new sequence's frames only
+            ref = full_sequence_output(n0, C, qa, ka, v, committed_k, committed_v, S, W, ft)
+            assert np.allclose(oa, ref, atol=1e-12, rtol=0)
+        assert used.commit(k, v, C) == fresh.commit(k, v, C)
+        committed_k[n0], committed_v[n0] = ka, v
+        assert used.retained() == fresh.retained()
+        assert all(t == t0 + f for f, _, t in used.retained())
+        assert sorted(used.cache) == [f for f, _, _ in used.retained()]

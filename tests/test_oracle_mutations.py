@@ -250,6 +250,20 @@ def _commit(evict_newest=False, highest_free=False, evict_sinks=False):
     return commit
 
 
+def _reset_keeps_t0(self, t0=0):
+    self.ring.reset()
+    self.cache = {}
+
+
+def _reset_keeps_cache(self, t0=0):
+    self.t0 = t0
+
+
+def _reset_keeps_cache_entries(self, t0=0):
+    self.ring.reset()
+    self.t0 = t0
+
+
 ROPE, ATT, RING = [pins_rope], [pins_attention], [pins_ring]
 
 MUTATIONS = {
@@ -282,6 +296,9 @@ MUTATIONS = {
     "masked formulation: window one frame long": (ATT, [(attention, "frame_visible", _frame_visible_window_long)]),
     "rollout: positions one frame late": (ATT, [(Rollout, "t_of", _t_of_plus_one)]),
     "rollout: chunk values shifted by a frame": (ATT, [(Rollout, "keys_values", _keys_values_own_chunk_first)]),
+    "rollout: reset keeps the old origin t0": (ATT, [(Rollout, "reset", _reset_keeps_t0)]),
+    "rollout: reset keeps the cache": (ATT, [(Rollout, "reset", _reset_keeps_cache)]),
+    "rollout: reset keeps the old frames' K/V entries": (ATT, [(Rollout, "reset", _reset_keeps_cache_entries)]),
     "ring: evicts the newest frame": (RING, [(ring.DequeRing, "commit", _commit(evict_newest=True))]),
     "ring: highest free slot first": (RING, [(ring.DequeRing, "commit", _commit(highest_free=True))]),
     "ring: sinks evicted like window frames": (RING, [(ring.DequeRing, "commit", _commit(evict_sinks=True))]),
