@@ -25,7 +25,7 @@ STATUS = {0: "WM_OK", 1: "WM_E_ARG", 2: "WM_E_SHAPE", 3: "WM_E_STATE", 4: "WM_E_
 # Every symbol include/wm.h declares.
 EXPORTS = ["wm_kvring_pool_bytes", "wm_kvring_create", "wm_kvring_destroy", "wm_kvring_reset",
            "wm_kvring_view", "wm_rope3d", "wm_rope3d_pair", "wm_chunk_attn", "wm_chunk_attn_layer",
-           "wm_chunk_attn_workspace_bytes",
+           "wm_chunk_attn_workspace_bytes", "wm_chunk_attn_noalloc",
            "wm_kvring_append_evict", "wm_rollout_step", "wm_rollout_graph_create",
            "wm_rollout_graph_launch", "wm_rollout_graph_destroy", "wm_last_error"]
 
@@ -81,6 +81,7 @@ def lib():
         L.wm_rope3d_pair.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, vp, vp, vp]
         L.wm_chunk_attn.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.c_float, vp, vp, sz, vp]
         L.wm_chunk_attn_layer.argtypes = [vp, i32, vp, vp, vp, i32, vp, ctypes.c_float, vp, vp, sz, vp]
+        L.wm_chunk_attn_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.c_float, vp, vp]
         L.wm_chunk_attn_workspace_bytes.argtypes = [vp, i32]
         L.wm_chunk_attn_workspace_bytes.restype = sz
         L.wm_kvring_append_evict.argtypes = [vp, vp, vp, i32, vp, vp, vp]
@@ -253,6 +254,21 @@ class KVRing:
                                          _ptr(k_rot, "k_rot", numel=nk_el), _ptr(v, "v", numel=nk_el),
                                          n_frames, act, float(scale), _ptr(out, "out", numel=nq_el),
                                          ws, ws_bytes, _stream(stream)))
+        return out
+
+    def chunk_attn_noalloc(self, q_rot, k_rot, v, n_frames, out=None, active=None, scale=0.0,
+                           stream=None):
+        """chunk_attn without a caller workspace: split partials go to the
+        library's static per-GPU scratch (calls that overlap on a GPU race)."""
+        if out is None:
+            out = torch.empty_like(q_rot)
+        nq_el = self.tokens(n_frames, self.hq)
+        nk_el = self.tokens(n_frames, self.hkv)
+        act_arr, act = _active(active, self.batch)
+        _check(lib().wm_chunk_attn_noalloc(self._h, _ptr(q_rot, "q_rot", numel=nq_el),
+                                           _ptr(k_rot, "k_rot", numel=nk_el), _ptr(v, "v", numel=nk_el),
+                                           n_frames, act, float(scale), _ptr(out, "out", numel=nq_el),
+                                           _stream(stream)))
         return out
 
     def append_evict(self, k_raw, v, n_frames, active=None, stream=None):

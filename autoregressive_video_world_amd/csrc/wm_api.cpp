@@ -538,6 +538,47 @@ int wg_per_bg_of(const wm_kvring* r, int n_frames) {
   return (group * task_blocks_of(r, n_frames) + waves - 1) / waves;
 }
 
+// The attention launch groups of a call: up to kAttnMaxB active rollouts each,
+// in batch order, with the split each would take given unlimited workspace.
+struct AttnGroup {
+  int nb = 0;
+  int max_ring = 0;
+  int nsplit = 1;
+  int32_t b_index[wm::kAttnMaxB];
+  int32_t n_ring[wm::kAttnMaxB];
+};
+
+std::vector<AttnGroup> attn_groups(const wm_kvring* r, int n_frames, const uint8_t* active) {
+  const wm_kvring_desc& d = r->desc;
+  std::vector<AttnGroup> groups;
+  AttnGroup g;
+  auto close = [&]() {
+    const int ntiles = ((g.max_ring + n_frames) * r->ft + 63) / 64;
+    g.nsplit = choose_split(g.nb * d.n_kv_heads * wg_per_bg_of(r, n_frames), ntiles);
+    groups.push_back(g);
+    g = AttnGroup();
+  };
+  for (int b = 0; b < d.batch; ++b) {
+    if (!is_active(active, b)) continue;
+    g.b_index[g.nb] = b;
+    g.n_ring[g.nb] = (int32_t)std::min<int64_t>(r->n_committed[b], r->R);
+    g.max_ring = std::max(g.max_ring, (int)g.n_ring[g.nb]);
+    if (++g.nb == wm::kAttnMaxB) close();
+  }
+  if (g.nb) close();
+  return groups;
+}
+
+// Workspace the largest group of a call needs for its split (0: no split).
+size_t attn_ws_needed(const wm_kvring* r, int n_frames, const std::vector<AttnGroup>& groups) {
+  size_t need = 0;
+  for (const AttnGroup& g : groups)
+    if (g.nsplit > 1)
+      need = std::max(need, split_ws_bytes(g.nsplit, g.nb, n_frames * r->ft, r->desc.n_q_heads,
+                                           r->desc.head_dim));
+  return need;
+}
+
 wm_status do_attn(const wm_kvring* r, int layer, const wm_bf16* q, const wm_bf16* kc,
                   const wm_bf16* vc, int n_frames, const uint8_t* active, float scale,
                   wm_bf16* out, void* ws, size_t ws_bytes, Sink& k) {
@@ -559,38 +600,26 @@ wm_status do_attn(const wm_kvring* r, int layer, const wm_bf16* q, const wm_bf16
   p.wave_qblocks = kWaveQBlocks;
   p.nqb = task_blocks_of(r, n_frames);
   p.wg_per_bg = wg_per_bg_of(r, n_frames);
-  p.nsplit = 1;
   const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)d.head_dim));
   p.scale_log2e = (float)((double)sc * 1.4426950408889634);
-  // Launch one group of rollouts, split when it pays and the workspace fits.
-  auto launch = [&](int max_ring) {
-    const int ntiles = ((max_ring + n_frames) * r->ft + 63) / 64;
-    int ns = choose_split(p.nb * p.hkv * p.wg_per_bg, ntiles);
+  // One launch per group of rollouts, split when it pays and the workspace
+  // fits (a split that does not fit is reduced until it does).
+  for (const AttnGroup& g : attn_groups(r, n_frames, active)) {
+    p.nb = g.nb;
+    memcpy(p.b_index, g.b_index, sizeof(int32_t) * g.nb);
+    memcpy(p.n_ring, g.n_ring, sizeof(int32_t) * g.nb);
+    int ns = g.nsplit;
     while (ns > 1 && (!ws || split_ws_bytes(ns, p.nb, p.nq, p.hq, d.head_dim) > ws_bytes)) --ns;
     p.nsplit = ns;
+    p.part_o = nullptr;
+    p.part_ml = nullptr;
     if (ns > 1) {
       const size_t rows = (size_t)ns * p.nb * p.nq * p.hq;
       p.part_o = static_cast<float*>(ws);
       p.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                            align_up(rows * d.head_dim * sizeof(float), 256));
     }
-    return k.attn(p, d.head_dim);
-  };
-  int max_ring = 0;
-  for (int b = 0; b < d.batch; ++b) {
-    if (!is_active(active, b)) continue;
-    p.b_index[p.nb] = b;
-    p.n_ring[p.nb] = (int32_t)std::min<int64_t>(r->n_committed[b], r->R);
-    max_ring = std::max(max_ring, (int)p.n_ring[p.nb]);
-    if (++p.nb == wm::kAttnMaxB) {
-      hipError_t e = launch(max_ring);
-      if (e != hipSuccess) return hip_fail(e, "chunk_attn launch");
-      p.nb = 0;
-      max_ring = 0;
-    }
-  }
-  if (p.nb) {
-    hipError_t e = launch(max_ring);
+    hipError_t e = k.attn(p, d.head_dim);
     if (e != hipSuccess) return hip_fail(e, "chunk_attn launch");
   }
   return WM_OK;
@@ -729,6 +758,23 @@ void drop_graph(wm_rollout_graph* g) {
 }
 
 // Arguments of wm_rope3d (for each tensor of wm_rope3d_pair).
+// Arguments of an attention call (everything but the workspace).
+wm_status check_attn(const wm_kvring* ring, int layer, const wm_bf16* q_rot, const wm_bf16* k_rot,
+                     const wm_bf16* v, int n_frames, float softmax_scale, const wm_bf16* out) {
+  wm_status st;
+  if ((st = check_ring(ring)) != WM_OK) return st;
+  if (layer < 0 || layer >= ring->n_layers)
+    return fail(WM_E_ARG, "layer %d not in [0, %d)", layer, ring->n_layers);
+  if ((st = check_device_ring(ring)) != WM_OK) return st;
+  if ((st = check_dev(q_rot, "q_rot")) != WM_OK) return st;
+  if ((st = check_dev(k_rot, "k_rot")) != WM_OK) return st;
+  if ((st = check_dev(v, "v")) != WM_OK) return st;
+  if ((st = check_dev(out, "out")) != WM_OK) return st;
+  if ((st = check_frames(ring, n_frames)) != WM_OK) return st;
+  if (!isfinite(softmax_scale)) return fail(WM_E_ARG, "softmax_scale is not finite");
+  return WM_OK;
+}
+
 wm_status check_rope(const wm_kvring* ring, const wm_bf16* x, wm_bf16* y, int32_t n_heads,
                      int32_t n_frames, const int64_t* t_first, const uint8_t* active) {
   wm_status st;
@@ -916,22 +962,40 @@ wm_status wm_chunk_attn_layer(const wm_kvring* ring, int32_t layer, const wm_bf1
                               const uint8_t* active, float softmax_scale, wm_bf16* out,
                               void* workspace, size_t workspace_bytes, void* stream) {
   wm_status st;
-  if ((st = check_ring(ring)) != WM_OK) return st;
-  if (layer < 0 || layer >= ring->n_layers)
-    return fail(WM_E_ARG, "layer %d not in [0, %d)", layer, ring->n_layers);
-  if ((st = check_device_ring(ring)) != WM_OK) return st;
-  if ((st = check_dev(q_rot, "q_rot")) != WM_OK) return st;
-  if ((st = check_dev(k_rot, "k_rot")) != WM_OK) return st;
-  if ((st = check_dev(v, "v")) != WM_OK) return st;
-  if ((st = check_dev(out, "out")) != WM_OK) return st;
-  if ((st = check_frames(ring, n_frames)) != WM_OK) return st;
+  if ((st = check_attn(ring, layer, q_rot, k_rot, v, n_frames, softmax_scale, out)) != WM_OK)
+    return st;
   if (workspace && !aligned16(workspace)) return fail(WM_E_ARG, "workspace is not 16-byte aligned");
-  if (!isfinite(softmax_scale)) return fail(WM_E_ARG, "softmax_scale is not finite");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = wait_finalize(ring, s)) != WM_OK) return st;
   Sink k{s};
   st = do_attn(ring, layer, q_rot, k_rot, v, n_frames, active, softmax_scale, out, workspace,
                workspace_bytes, k);
+  if (st != WM_OK) return st;
+  return finish(s);
+}
+
+static_assert(wm::kScratchBytes == WM_NOALLOC_SCRATCH_BYTES, "scratch size");
+
+wm_status wm_chunk_attn_noalloc(const wm_kvring* ring, const wm_bf16* q_rot, const wm_bf16* k_rot,
+                                const wm_bf16* v, int32_t n_frames, const uint8_t* active,
+                                float softmax_scale, wm_bf16* out, void* stream) {
+  wm_status st;
+  if ((st = check_attn(ring, 0, q_rot, k_rot, v, n_frames, softmax_scale, out)) != WM_OK) return st;
+  // The split wm_chunk_attn takes with a large enough workspace, or an error.
+  const size_t need = attn_ws_needed(ring, n_frames, attn_groups(ring, n_frames, active));
+  if (need > wm::kScratchBytes)
+    return fail(WM_E_CAPACITY,
+                "this call's key-range split needs %zu bytes of scratch, more than the %zu the "
+                "allocation-free entry point holds per device (use wm_chunk_attn with a workspace)",
+                need, wm::kScratchBytes);
+  void* scratch = nullptr;
+  hipError_t e = wm::scratch_region(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "scratch address (hipGetSymbolAddress)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = wait_finalize(ring, s)) != WM_OK) return st;
+  Sink k{s};
+  st = do_attn(ring, 0, q_rot, k_rot, v, n_frames, active, softmax_scale, out, scratch,
+               wm::kScratchBytes, k);
   if (st != WM_OK) return st;
   return finish(s);
 }

@@ -105,6 +105,15 @@ struct AttnParams {
   int32_t n_ring[kAttnMaxB];   // visible ring frames (slots 0 .. n_ring-1)
 };
 
+// Scratch of the allocation-free attention entry point (key-range split
+// partials), one static device array per GPU; equal to the public
+// WM_NOALLOC_SCRATCH_BYTES.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+
+// This device's address of that array: looked up with hipGetSymbolAddress on
+// the first call with the device current, then cached per device.
+hipError_t scratch_region(void** ptr);
+
 // Launches of one attention group: fills p's derived fields (workgroup count,
 // XCD stride) and returns the attention launch and, when the key range is
 // split, the combine launch (both take p); 0 if the shape is not built.

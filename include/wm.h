@@ -270,6 +270,31 @@ wm_status wm_chunk_attn_layer(const wm_kvring* ring, int32_t layer, const wm_bf1
 size_t wm_chunk_attn_workspace_bytes(const wm_kvring* ring, int32_t n_frames);
 
 /* ---------------------------------------------------------------------------
+ * Allocation-free attention: for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The caller still passes the inputs and the output.
+ *
+ * Computes exactly what wm_chunk_attn (layer 0) computes with a workspace of
+ * at least wm_chunk_attn_workspace_bytes(): the same launches with the same
+ * key-range split, hence the same output bits.  The split partials live in a
+ * static device array of WM_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends; its device address is looked
+ * up once per device (the first call with that device current).  The call
+ * allocates nothing (no hipMalloc/hipFree, no allocating library routine).
+ * The array needs no clearing: every split partial a launch reads was
+ * written by that launch.
+ * All calls on one GPU share that GPU's array and it keeps the last call's
+ * contents: calls that can overlap on one GPU (other streams, other threads,
+ * other rings) race on it and must be ordered by the caller.
+ * Errors: as wm_chunk_attn; WM_E_CAPACITY (nothing enqueued) when the call's
+ * split needs more than WM_NOALLOC_SCRATCH_BYTES (e.g. many rollouts with
+ * long key ranges): use wm_chunk_attn with a workspace there. */
+#define WM_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+wm_status wm_chunk_attn_noalloc(const wm_kvring* ring, const wm_bf16* q_rot, const wm_bf16* k_rot,
+                                const wm_bf16* v, int32_t n_frames, const uint8_t* active,
+                                float softmax_scale, wm_bf16* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Append + evict (FlashDreams finalize()).
  *
  * Commits n_frames frames to every active rollout: frame ids n_committed ..
