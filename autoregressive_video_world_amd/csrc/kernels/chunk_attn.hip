@@ -12,7 +12,15 @@
 // (row stride Hkv*d).  Softmax is order-invariant, so keys are visited in
 // slot order, never concatenated.
 //
-// Design (one workgroup = 4 waves = 4 "wave tasks" that share one kv head):
+// Two forms share this file's helpers and the key-range split/combine:
+//  * chunk_attn8_kernel (the one launched): eight waves per workgroup, two per
+//    SIMD, 32 queries per wave -- described where it is defined below;
+//  * chunk_attn_kernel: four waves, one per SIMD, 64 queries per wave
+//    (selectable with WM_ATTN_FORM=4 for measurement), described here.
+// Both cover 256 queries of one kv head per workgroup.
+//
+// Design of the four-wave form (one workgroup = 4 waves = 4 "wave tasks"
+// that share one kv head):
 //  * a wave task is 64 queries of one q head: two 32-query blocks;
 //  * keys stream through LDS in 64-key tiles, K and V triple-buffered, with
 //    direct global->LDS loads (global_load_lds_dwordx4): no staging
@@ -50,6 +58,7 @@
 #include "../wm_internal.hpp"
 
 #include <mutex>
+#include <type_traits>
 
 namespace wm {
 namespace {
@@ -616,6 +625,377 @@ __global__ __launch_bounds__(512 / NQB, 1) void chunk_attn_kernel(const AttnPara
   }
 }
 
+// ---------------------------------------------------------------------------
+// Eight-wave form: two waves per SIMD, 32 queries per wave.
+//
+// One wave issues at most one vector instruction every ~5 cycles (an exp
+// every ~10), so the ~100 softmax instructions that go with every 16 MFMAs of
+// a 64-query wave cannot hide under its own 512 MFMA cycles.  With two waves
+// per SIMD each wave has half the queries and half the vector work, and the
+// SIMD issues both waves' vector instructions beside the other wave's MFMAs.
+// Each K or V fragment read from LDS then feeds one MFMA instead of two,
+// which the LDS read rate (~245 B/clk per CU for 16-byte reads) carries.
+// Per wave and 32-key sub-tile j:
+//   QK half (one MFMA slot per 16-wide d chunk): S(j+1) = K Q^T on the
+//     matrix cores (K fragments already in registers) || P(j) = exp2(S(j)
+//     * scale - m) on the vector ALUs || the V^T fragments of sub-tile j
+//     read from LDS;
+//   PV half (one slot per V fragment): O^T += V^T P(j)^T || the row max of
+//     S(j+1) || the K fragments of sub-tile j+2 read from LDS.
+// Every operand and accumulator lives in VGPRs (230 of the 256 a wave has at
+// two waves per SIMD; no AGPRs), so the softmax reads S without accumulator
+// copies.  Tiles of 64 keys stream through NBUF LDS buffers; one
+// barrier per tile, in the middle of its first sub-step, after which the
+// DMA of the tile NBUF-1 ahead is issued into the buffer the tile before
+// freed.
+// ---------------------------------------------------------------------------
+template <int HD>
+struct Cfg8 {
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int NDC = HD / 16;             // QK MFMAs per sub-tile
+  static constexpr int NDB = HD / 32;             // 32-row d blocks of O^T
+  static constexpr int NCOL = HD / 8;             // 16-byte columns per key row
+  static constexpr int COLS_PER_WAVE = NCOL / WAVES;
+  static constexpr int TILE_BYTES = NCOL * kColPitch;
+  static_assert(COLS_PER_WAVE >= 1, "every wave fills at least one column");
+};
+
+template <int HD, int NBUF>
+__global__ __launch_bounds__(512, 1) void chunk_attn8_kernel(const AttnParams p) {
+  using C = Cfg8<HD>;
+  static_assert(NBUF == 3 || NBUF == 4, "three or four tile buffers");
+  // Distinct LDS objects: a read of one buffer provably never aliases a DMA
+  // still writing another, so reads do not wait for every pending DMA.
+  __shared__ __attribute__((aligned(16))) uint8_t k0s[C::TILE_BYTES], k1s[C::TILE_BYTES], k2s[C::TILE_BYTES],
+      k3s[NBUF == 4 ? C::TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t v0s[C::TILE_BYTES], v1s[C::TILE_BYTES], v2s[C::TILE_BYTES],
+      v3s[NBUF == 4 ? C::TILE_BYTES : 16];
+  lds_u8* const KB[4] = {(lds_u8*)k0s, (lds_u8*)k1s, (lds_u8*)k2s, (lds_u8*)k3s};
+  lds_u8* const VB[4] = {(lds_u8*)v0s, (lds_u8*)v1s, (lds_u8*)v2s, (lds_u8*)v3s};
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  int bid = (int)(blockIdx.x % kXcds) * p.per_xcd + (int)(blockIdx.x / kXcds);
+  if (bid >= p.n_wg) return;
+  const int split = bid % p.nsplit;
+  bid /= p.nsplit;
+  const int wgi = bid % p.wg_per_bg;
+  bid /= p.wg_per_bg;
+  const int g = bid % p.hkv;
+  const int bi = bid / p.hkv;
+  const int b = p.b_index[bi];
+  const int ring_keys = p.n_ring[bi] * p.ft;
+  const int nk = ring_keys + p.nq;
+  const int ntiles = (nk + kKT - 1) / kKT;
+  const int tps = (ntiles + p.nsplit - 1) / p.nsplit;
+  const int t_begin = split * tps;
+  const int n_local = min(ntiles, t_begin + tps) - t_begin;
+
+  const int task = wgi * C::WAVES + wave;
+  const bool has_task = task < p.group * p.nqb;
+  const int qblk = has_task ? task / p.group : 0;
+  const int h = g * p.group + (has_task ? task % p.group : 0);
+  const int q0 = qblk * 32;
+
+  if (n_local <= 0) {
+    if (has_task && lane < 32) {
+      const int q = q0 + lane;
+      if (q < p.nq) {
+        const int64_t row = (((int64_t)split * p.nb + bi) * p.nq + q) * p.hq + h;
+        p.part_ml[row * 2 + 0] = -INFINITY;
+        p.part_ml[row * 2 + 1] = 0.f;
+      }
+    }
+    return;
+  }
+
+  // Q^T operands: lane (l32, hi) holds query q0+l32, d = dc*16 + hi*8 .. +8.
+  bf16x8 qreg[C::NDC];
+  {
+    const int q = min(q0 + l32, p.nq - 1);
+    const uint16_t* src = p.q + (((int64_t)b * p.nq + q) * p.hq + h) * HD + hi * 8;
+#pragma unroll
+    for (int dc = 0; dc < C::NDC; ++dc) {
+      qreg[dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src + dc * 16));
+    }
+  }
+
+  // ---- tile loads: lane = key row, wave w fills columns w*CPW .. ---------
+  const int ft = p.ft;
+  const float inv_ft = 1.0f / (float)ft;
+  const int col0 = __builtin_amdgcn_readfirstlane(wave) * C::COLS_PER_WAVE;
+  const uint16_t* const ring_k = p.pk + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD + col0 * 8;
+  const uint16_t* const ring_v = p.pv + ((int64_t)b * p.ring_slots * p.hkv + g) * (int64_t)ft * HD + col0 * 8;
+  const uint32_t slot_stride = (uint32_t)p.hkv * ft * HD;
+  const uint16_t* const chunk_k = p.kc + ((int64_t)b * p.nq * p.hkv + g) * HD + col0 * 8;
+  const uint16_t* const chunk_v = p.vc + ((int64_t)b * p.nq * p.hkv + g) * HD + col0 * 8;
+  const uint32_t chunk_stride = (uint32_t)p.hkv * HD;
+
+  // Tile loads: direct global->LDS DMA, lane = key row, wave w fills the
+  // 16-byte columns w*CPW .. of K and of V (keys past the end clamp to the
+  // last key).  A tile's DMA instructions are spread over the slots of two
+  // sub-steps instead of issued together: the row addresses are formed once
+  // (tile_rows), then each call of dma_col issues one column.
+  const uint16_t* dkp;  // this lane's K and V row of the tile being fetched
+  const uint16_t* dvp;
+  auto tile_rows = [&](int u) __attribute__((always_inline)) {
+    const int j = min((t_begin + u) * kKT + lane, nk - 1);
+    int s = (int)((float)j * inv_ft);
+    int r = j - s * ft;
+    s += (r >= ft) - (r < 0);
+    r = j - s * ft;
+    const bool in_ring = j < ring_keys;
+    const uint32_t ro = (uint32_t)s * slot_stride + (uint32_t)r * HD;
+    const uint32_t co = (uint32_t)(j - ring_keys) * chunk_stride;
+    dkp = in_ring ? ring_k + ro : chunk_k + co;
+    dvp = in_ring ? ring_v + ro : chunk_v + co;
+  };
+  // column c of this wave's share (c < CPW: K, else V) into tile kt / vt
+  auto dma_col = [&](int c, lds_u8* kt, lds_u8* vt) __attribute__((always_inline)) {
+    if (c < C::COLS_PER_WAVE) {
+      const uint16_t* src = dkp + c * 8;
+      lds_u8* dst = kt + (col0 + c) * kColPitch;
+      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    } else {
+      const uint16_t* src = dvp + (c - C::COLS_PER_WAVE) * 8;
+      lds_u8* dst = vt + (col0 + c - C::COLS_PER_WAVE) * kColPitch;
+      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    }
+  };
+  constexpr int NDMA = 2 * C::COLS_PER_WAVE;  // DMA instructions per wave per tile
+
+  // ---- running state ------------------------------------------------------
+  f32x16 oacc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // running max (scaled, log2), this lane's partial sum
+  const float sl2 = p.scale_log2e;
+
+  const uint32_t k_off = (uint32_t)(hi * kColPitch + l32 * 16);
+  const int tr_l = lane & 15;
+  const uint32_t v_off = (uint32_t)((((lane >> 4) & 1) * 2 + ((tr_l & 3) >> 1)) * kColPitch +
+                                    (hi * 4 + (tr_l >> 2)) * 16 + (tr_l & 1) * 8);
+
+  // K fragments of the next sub-tile's QK.
+  bf16x8 kf[C::NDC];
+  auto read_k = [&](const lds_u8* tile, int kb, int dc) __attribute__((always_inline)) {
+    kf[dc] = *(const lds_bf16x8*)(tile + k_off + 2 * dc * kColPitch + kb * 512);
+  };
+  auto rowmax16 = [&](const f32x16& S) __attribute__((always_inline)) {
+    float m0 = fmaxf(S[0], fmaxf(S[1], S[2]));
+    float m1 = fmaxf(S[3], fmaxf(S[4], S[5]));
+    m0 = fmaxf(m0, fmaxf(S[6], S[7]));
+    m1 = fmaxf(m1, fmaxf(S[8], S[9]));
+    m0 = fmaxf(m0, fmaxf(S[10], S[11]));
+    m1 = fmaxf(m1, fmaxf(S[12], S[13]));
+    m0 = fmaxf(m0, fmaxf(S[14], S[15]));
+    return xhalf_max(fmaxf(m0, m1));
+  };
+  const int nk_local = nk - t_begin * kKT;
+  // Mask keys past the end of the range (only in the last tile), then decide
+  // the lazy rescale for the sub-tile whose exponentials come next.  O is
+  // rescaled here, after the previous sub-tile's P*V (formed against the old
+  // max) was issued; the hardware orders the accumulator update after it.
+  auto prepare = [&](int j, f32x16& S, float mx) __attribute__((always_inline)) {
+    const int nvalid = nk_local - j * 32;
+    if (nvalid < 32) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = (i >> 2) * 8 + hi * 4 + (i & 3);
+        if (key >= nvalid) S[i] = -INFINITY;
+      }
+      mx = rowmax16(S);
+    }
+    const bool need = mx * sl2 > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = fmaxf(m_run, mx * sl2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      asm volatile("; rescale O" ::: "memory");
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      }
+    }
+  };
+
+  constexpr int NQK = C::NDC;       // QK slots
+  constexpr int NPV = 2 * C::NDB;   // PV slots (one per V fragment)
+  constexpr int NE = 8;             // exponential units (2 keys each) per sub-tile
+  constexpr int E_PER = (NE + NQK - 1) / NQK;
+  constexpr int K_PER = (C::NDC + NPV - 1) / NPV;  // K fragment reads per PV slot
+  constexpr int MX0 = NPV >= 8 ? 2 : 1;            // first PV slot of the row max
+  constexpr int MX_UNITS = 4;                      // 4 values each
+  constexpr int MX_PER = (MX_UNITS + (NPV - MX0) - 1) / (NPV - MX0);
+
+  // One sub-step j: Sc = S(j) (already masked and max-checked), Sn receives
+  // S(j+1); vt/vkb: V of sub-tile j; kt2/kb2: K of sub-tile j+2; mid(): the
+  // tile barrier and DMA issue between the halves (or nothing).  Returns the
+  // row max of S(j+1).
+  auto substep = [&](const f32x16& Sc, f32x16& Sn, const lds_u8* vt, int vkb, const lds_u8* kt2,
+                     int kb2, auto&& mid, auto&& slot_hook) __attribute__((always_inline)) {
+    bf16x8 vfr[NPV];
+    uint32_t pk[8];
+    const float mneg = -m_run;
+    auto read_v = [&](int f) __attribute__((always_inline)) {  // f = half * NDB + db
+      const int half = f / C::NDB, db = f % C::NDB;
+      const lds_u8* a = vt + v_off + db * 4 * kColPitch + (vkb * 32 + half * 16) * 16;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
+      const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * 16));
+      vfr[f] = __builtin_bit_cast(bf16x8, (s16x8){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+    };
+    auto exp_unit = [&](int e) __attribute__((always_inline)) {
+      float s0 = Sc[2 * e], s1 = Sc[2 * e + 1];
+      asm volatile("" : "+v"(s0), "+v"(s1));
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, sl2, mneg));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, sl2, mneg));
+      const bf16x2 two = {(__bf16)e0, (__bf16)e1};
+      l_run = (l_run + e0) + e1;
+      pk[e] = __builtin_bit_cast(uint32_t, two);
+      asm volatile("" ::"v"(pk[e]), "v"(l_run));
+    };
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qreg[i], i == 0 ? (f32x16){} : Sn, 0, 0, 0);
+#pragma unroll
+      for (int f = i * NPV / NQK; f < (i + 1) * NPV / NQK; ++f) read_v(f);
+#pragma unroll
+      for (int k = 0; k < E_PER; ++k)
+        if (i * E_PER + k < NE) exp_unit(i * E_PER + k);
+      slot_hook(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const bf16x8 P0 = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    const bf16x8 P1 = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
+    mid();
+    __builtin_amdgcn_sched_barrier(0);
+    float mq[MX_UNITS];
+    float mx = 0.f;
+#pragma unroll
+    for (int m = 0; m < NPV; ++m) {
+      const int half = m / C::NDB, db = m % C::NDB;
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[m], half ? P1 : P0, oacc[db], 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < K_PER; ++k)
+        if (m * K_PER + k < C::NDC) read_k(kt2, kb2, m * K_PER + k);
+#pragma unroll
+      for (int k = 0; k < MX_PER; ++k) {
+        const int t = (m - MX0) * MX_PER + k;
+        if (m >= MX0 && t < MX_UNITS) {
+          mq[t] = fmaxf(fmaxf(Sn[4 * t], Sn[4 * t + 1]), fmaxf(Sn[4 * t + 2], Sn[4 * t + 3]));
+          asm volatile("" ::"v"(mq[t]));
+          if (t == MX_UNITS - 1) {
+            mx = xhalf_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
+            asm volatile("" ::"v"(mx));
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return mx;
+  };
+
+  // ---- prologue: tiles 0 .. NBUF-2 in flight; S(0) and its row max --------
+#pragma unroll
+  for (int u = 0; u < NBUF - 1; ++u) {
+    tile_rows(u);
+#pragma unroll
+    for (int c = 0; c < NDMA; ++c) dma_col(c, KB[u], VB[u]);
+  }
+  wait_vmcnt<(NBUF - 2) * NDMA>();
+  tile_barrier<(NBUF - 2) * NDMA>();
+  f32x16 SA, SB;
+#pragma unroll
+  for (int dc = 0; dc < C::NDC; ++dc) read_k(KB[0], 0, dc);
+#pragma unroll
+  for (int dc = 0; dc < C::NDC; ++dc) {
+    SA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dc], qreg[dc], dc == 0 ? (f32x16){} : SA, 0, 0, 0);
+  }
+#pragma unroll
+  for (int dc = 0; dc < C::NDC; ++dc) read_k(KB[0], 1, dc);
+  prepare(0, SA, rowmax16(SA));
+
+  // Sub-steps 2u and 2u+1 of local tile u (buffer u % NBUF).  The barrier in
+  // the middle of sub-step 2u: this wave's DMA of tile u+1 has landed, every
+  // wave is done with tile u-1.  After it the DMA of tile u+NBUF-1, into the
+  // buffer tile u-1 left, is issued one column per QK slot across sub-step
+  // 2u+1 (only the DMA of tile u+NBUF-2 may then be in flight at the next
+  // barrier when NBUF = 4; NBUF = 3 waits for everything).
+  auto tile_steps = [&](int u, auto ph_) __attribute__((always_inline)) {
+    constexpr int ph = decltype(ph_)::value;
+    constexpr int nx = (ph + 1) % NBUF;
+    constexpr int fr = (ph + NBUF - 1) % NBUF;
+    float mx = substep(SA, SB, VB[ph], 0, KB[nx], 0, [&]() __attribute__((always_inline)) {
+      tile_barrier<(NBUF - 3) * NDMA>();
+      tile_rows(u + NBUF - 1);
+    }, [](int) {});
+    prepare(2 * u + 1, SB, mx);
+    mx = substep(SB, SA, VB[ph], 1, KB[nx], 1, []() {}, [&](int i) __attribute__((always_inline)) {
+      constexpr int every = NQK / NDMA;
+      if (i % every == every - 1) dma_col(i / every, KB[fr], VB[fr]);
+    });
+    prepare(2 * u + 2, SA, mx);
+  };
+  int u = 0;
+  for (; u + NBUF <= n_local; u += NBUF) {
+    tile_steps(u, std::integral_constant<int, 0>{});
+    tile_steps(u + 1, std::integral_constant<int, 1>{});
+    tile_steps(u + 2, std::integral_constant<int, 2>{});
+    if constexpr (NBUF == 4) tile_steps(u + 3, std::integral_constant<int, 3>{});
+  }
+  if (u < n_local) tile_steps(u++, std::integral_constant<int, 0>{});
+  if (u < n_local) tile_steps(u++, std::integral_constant<int, 1>{});
+  if constexpr (NBUF == 4)
+    if (u < n_local) tile_steps(u++, std::integral_constant<int, 2>{});
+  // No DMA may still be writing this workgroup's LDS when it retires.
+  wait_vmcnt<0>();
+
+  if (!has_task) return;
+
+  // ---- epilogue -------------------------------------------------------------
+  const int q = q0 + l32;
+  const float l_tot = xhalf_sum(l_run);
+  if (q >= p.nq) return;
+  const float inv = 1.0f / l_tot;
+  if (p.nsplit == 1) {
+    uint16_t* dst = p.out + (((int64_t)b * p.nq + q) * p.hq + h) * HD;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int d = db * 32 + ii * 8 + hi * 4;
+        const uint2 v = make_uint2(pack_bf16(oacc[db][ii * 4 + 0] * inv, oacc[db][ii * 4 + 1] * inv),
+                                   pack_bf16(oacc[db][ii * 4 + 2] * inv, oacc[db][ii * 4 + 3] * inv));
+        *reinterpret_cast<uint2*>(dst + d) = v;
+      }
+  } else {
+    const int64_t row = (((int64_t)split * p.nb + bi) * p.nq + q) * p.hq + h;
+    float* dst = p.part_o + row * HD;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int d = db * 32 + ii * 8 + hi * 4;
+        *reinterpret_cast<float4*>(dst + d) =
+            make_float4(oacc[db][ii * 4 + 0] * inv, oacc[db][ii * 4 + 1] * inv,
+                        oacc[db][ii * 4 + 2] * inv, oacc[db][ii * 4 + 3] * inv);
+      }
+    if (hi == 0) {
+      p.part_ml[row * 2 + 0] = m_run;
+      p.part_ml[row * 2 + 1] = l_tot;
+    }
+  }
+}
+
 // Merge the key-range partials of a split launch: weights l_s * 2^(m_s - M)
 // over the splits with keys (log-sum-exp combine), one thread per 8 output
 // dims of one (rollout, query, head) row.
@@ -707,13 +1087,23 @@ hipError_t scratch_region(void** ptr) {
 }
 
 int chunk_attn_specs(AttnParams& p, int head_dim, LaunchSpec specs[2]) {
-  if (p.wave_qblocks != 2 || (head_dim != 128 && head_dim != 64)) return 0;
+  if ((p.wave_qblocks != 1 && p.wave_qblocks != 2) || (head_dim != 128 && head_dim != 64)) return 0;
   p.n_wg = p.nb * p.hkv * p.wg_per_bg * p.nsplit;
   p.per_xcd = (p.n_wg + kXcds - 1) / kXcds;
   specs[0].grid = dim3(p.per_xcd * kXcds);
-  specs[0].block = dim3(Cfg<128, 2>::THREADS);
-  specs[0].func = head_dim == 128 ? reinterpret_cast<const void*>(&chunk_attn_kernel<128, 2>)
-                                  : reinterpret_cast<const void*>(&chunk_attn_kernel<64, 2>);
+  if (p.wave_qblocks == 1) {
+    specs[0].block = dim3(Cfg8<128>::THREADS);
+    if (p.tile_bufs == 4)
+      specs[0].func = head_dim == 128 ? reinterpret_cast<const void*>(&chunk_attn8_kernel<128, 4>)
+                                      : reinterpret_cast<const void*>(&chunk_attn8_kernel<64, 4>);
+    else
+      specs[0].func = head_dim == 128 ? reinterpret_cast<const void*>(&chunk_attn8_kernel<128, 3>)
+                                      : reinterpret_cast<const void*>(&chunk_attn8_kernel<64, 3>);
+  } else {
+    specs[0].block = dim3(Cfg<128, 2>::THREADS);
+    specs[0].func = head_dim == 128 ? reinterpret_cast<const void*>(&chunk_attn_kernel<128, 2>)
+                                    : reinterpret_cast<const void*>(&chunk_attn_kernel<64, 2>);
+  }
   if (p.nsplit == 1) return 1;
   const int64_t threads = (int64_t)p.nb * p.nq * p.hq * (head_dim / 8);
   specs[1].grid = dim3((unsigned)((threads + 255) / 256));

@@ -521,20 +521,29 @@ size_t split_ws_bytes(int nsplit, int nb, int nq, int hq, int hd) {
   return align_up(rows * hd * sizeof(float), 256) + rows * 2 * sizeof(float);
 }
 
-// Attention wave tasks: 32-query blocks per wave.  2 = four waves per
-// workgroup, one per SIMD, 64 queries each (the launched form; eight waves of
-// 32 queries, two per SIMD, measured ~10% slower at d = 128: every K/V
-// fragment read from LDS then feeds half as many MFMAs).
-constexpr int kWaveQBlocks = 2;
+// Attention wave tasks: 32-query blocks per wave.  1 = eight waves per
+// workgroup, two per SIMD, 32 queries each; 2 = four waves, one per SIMD,
+// 64 queries each.  Either way a workgroup covers 256 queries of one kv head.
+// WM_ATTN_FORM=4 selects the four-wave form and WM_ATTN_BUFS=3 three LDS tile
+// buffers (instead of four) in the eight-wave form (measurement).
+int wave_qblocks() {
+  const char* e = getenv("WM_ATTN_FORM");
+  return (e && atoi(e) == 4) ? 2 : 1;
+}
+
+int tile_bufs() {
+  const char* e = getenv("WM_ATTN_BUFS");
+  return (e && atoi(e) == 3) ? 3 : 4;
+}
 
 int task_blocks_of(const wm_kvring* r, int n_frames) {
-  const int q_per_task = 32 * kWaveQBlocks;
+  const int q_per_task = 32 * wave_qblocks();
   return (n_frames * r->ft + q_per_task - 1) / q_per_task;
 }
 
 int wg_per_bg_of(const wm_kvring* r, int n_frames) {
   const int group = r->desc.n_q_heads / r->desc.n_kv_heads;
-  const int waves = 8 / kWaveQBlocks;
+  const int waves = 8 / wave_qblocks();
   return (group * task_blocks_of(r, n_frames) + waves - 1) / waves;
 }
 
@@ -597,7 +606,8 @@ wm_status do_attn(const wm_kvring* r, int layer, const wm_bf16* q, const wm_bf16
   p.ft = r->ft;
   p.nq = n_frames * r->ft;
   p.ring_slots = r->R;
-  p.wave_qblocks = kWaveQBlocks;
+  p.wave_qblocks = wave_qblocks();
+  p.tile_bufs = tile_bufs();
   p.nqb = task_blocks_of(r, n_frames);
   p.wg_per_bg = wg_per_bg_of(r, n_frames);
   const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)d.head_dim));

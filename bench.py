@@ -86,6 +86,14 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
+def attn_kernel_name(head_dim):
+    """The attention kernel the library launches (the eight-wave form unless
+    WM_ATTN_FORM=4 selects the four-wave one)."""
+    if os.environ.get("WM_ATTN_FORM") == "4":
+        return "chunk_attn_kernel<%d, 2>" % head_dim
+    return "chunk_attn8_kernel<%d, %d>" % (head_dim, 3 if os.environ.get("WM_ATTN_BUFS") == "3" else 4)
+
+
 def profiled_traffic(workload_name, key="traffic_bytes_per_launch"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
 
@@ -555,7 +563,7 @@ def main():
         "first_step_ms": round(first_step_ms, 3),
         "whole_rollout": rollout,
         "attn_pct_mfma_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "kernel": "chunk_attn_kernel<128>",
+        "roofline": {"bound": "mfma", "kernel": attn_kernel_name(wl.head_dim),
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": prof_traffic,
                      "launch_ms_mean": round(attn_mean, 4), "launch_ms_p50": round(attn_p50, 4),
