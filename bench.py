@@ -55,6 +55,10 @@ def parse():
                     help="time only the steady-state step and its kernels (no multi-layer append, "
                          "extra workloads, launch modes or whole rollout): every attention launch "
                          "then has the steady shape, as profiling runs want")
+    ap.add_argument("--append-sweep", default="1,2,4,8,16,30",
+                    help="layer counts of the append transfer-size sweep: one multi-layer append per "
+                         "count (57.5 MB per layer at sf13b), inputs from HBM, beside a plain copy of "
+                         "the same bytes (empty = skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain elementwise copy of this many MiB first (untimed), as the "
                          "known-size reference for HBM byte counters")
@@ -274,7 +278,7 @@ def rollout_modes(torch, wm, wl, randn, dev, steps, warmup, ring=None):
 def main():
     args = parse()
     if args.steady_only:
-        args.layers, args.extra_workloads, args.modes_workload = 0, "0", 0
+        args.layers, args.extra_workloads, args.modes_workload, args.append_sweep = 0, "0", 0, ""
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (it would shard by rollout "
               "or by kv head with no collective in the path); run with --gpus 1", file=sys.stderr)
@@ -479,6 +483,48 @@ def main():
         mring.close()
     torch.cuda.synchronize()
 
+    # Append transfer-size sweep: one append of L layers per launch (L x the
+    # workload's per-chunk bytes), inputs rotated over more than twice the
+    # 256 MB last-level cache so that they come from HBM, beside a plain
+    # elementwise copy (torch.neg) of exactly the same bytes rotated the same
+    # way -- where one transfer of this size tops out on this chip.
+    sweep = []
+    for Ln in [int(x) for x in args.append_sweep.split(",") if x.strip()]:
+        sring = wm.KVRing(1, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                          wl.n_sink, wl.window, wl.chunk, device=dev, n_layers=Ln, n_views=wl.n_views)
+        nbytes = Ln * wl.append_bytes()
+        nrot = max(2, -(-(512 << 20) // (nbytes // 2)))
+        sin = [(randn(Ln, *ks[-1].shape), randn(Ln, *vs[-1].shape)) for _ in range(nrot)]
+        si = [0]
+
+        def sweep_app():
+            kc, vc = sin[si[0] % nrot]
+            si[0] += 1
+            sring.append_evict(kc, vc, C)
+
+        reps = max(2 * nrot, 8)
+        a_mean, _ = timed(sweep_app, reps, busy)
+        del sin
+        csrc = [randn(nbytes // 4) for _ in range(nrot)]
+        cdst = [torch.empty_like(x) for x in csrc]
+        ci = [0]
+
+        def sweep_copy():
+            a = ci[0] % nrot
+            ci[0] += 1
+            torch.neg(csrc[a], out=cdst[a])
+
+        c_mean, _ = timed(sweep_copy, reps, busy)
+        del csrc, cdst
+        sring.close()
+        sweep.append({"layers": Ln, "bytes_per_launch": nbytes,
+                      "append_gbs": round(nbytes / (a_mean * 1e-3) / 1e9, 1),
+                      "append_frac": round(nbytes / (a_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "append_us": round(a_mean * 1e3, 2),
+                      "copy_gbs": round(nbytes / (c_mean * 1e-3) / 1e9, 1),
+                      "copy_us": round(c_mean * 1e3, 2)})
+    torch.cuda.synchronize()
+
     # Steady-state attention of other workloads: the same kernel at other
     # shapes, the key-range split and its combine where the grid is small
     # (launch time = attention + combine), several camera views per frame.
@@ -537,6 +583,7 @@ def main():
     copy_cold_gbs = app_bytes / (copy_cold_mean * 1e-3) / 1e9
     rope_bytes = 2 * wl.nq * wl.head_dim * 2 * (wl.n_q_heads + wl.n_kv_heads)
     rope_gbs = rope_bytes / (rope_mean * 1e-3) / 1e9
+    rope_cold_gbs = rope_bytes / (rope_cold_mean * 1e-3) / 1e9
     prof_traffic = profiled_traffic(wl.name)
 
     result = {
@@ -569,22 +616,29 @@ def main():
                      "launch_ms_mean": round(attn_mean, 4), "launch_ms_p50": round(attn_p50, 4),
                      "launch_ms_p90": round(attn_p90, 4),
                      "flops_per_launch": wl.attn_flops(), "split_workspace_bytes": ws_bytes},
-        "append": {"bound": "hbm", "achieved": round(app_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                   "frac": round(app_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": app_bytes,
+        "append": {"bound": "hbm", "inputs": "from HBM (rotated over 512 MB, twice the last-level cache)",
+                   "achieved": round(app_cold_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": round(app_cold_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": app_bytes,
                    "traffic": profiled_traffic(wl.name, "append_traffic_bytes_per_launch"),
-                   "launch_ms_mean": round(app_mean, 5), "host_us_per_call": round(app_host_us, 1),
-                   "achieved_inputs_from_hbm": round(app_cold_gbs, 1),
-                   "frac_inputs_from_hbm": round(app_cold_gbs / PEAK_HBM_GBS, 4),
-                   "copy_same_bytes_from_hbm": round(copy_cold_gbs, 1)},
+                   "launch_ms_mean": round(app_cold_mean, 5), "host_us_per_call": round(app_host_us, 1),
+                   "copy_same_bytes_from_hbm": round(copy_cold_gbs, 1),
+                   "frac_of_copy": round(app_cold_gbs / copy_cold_gbs, 4),
+                   "achieved_mall_warm": round(app_gbs, 1),
+                   "frac_mall_warm": round(app_gbs / PEAK_HBM_GBS, 4),
+                   "launch_ms_mean_mall_warm": round(app_mean, 5)},
+        "append_size_sweep": sweep,
         "rollout_modes": ([modes] if modes else []) + ([modes_small] if modes_small else []),
         "append_layers": layers,
         "other_workloads": extras,
-        "rope": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                 "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
-                 "launch_ms_mean": round(rope_mean, 5), "host_us_per_call": round(rope_host_us, 1),
-                 "achieved_inputs_from_hbm": round(rope_bytes / (rope_cold_mean * 1e-3) / 1e9, 1),
-                 "frac_inputs_from_hbm": round(rope_bytes / (rope_cold_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                 "q_and_k_as_two_launches_gbs": round(rope_bytes / ((rope_q_mean + rope_k_mean) * 1e-3) / 1e9, 1)},
+        "rope": {"bound": "hbm", "inputs": "from HBM (rotated over 512 MB, twice the last-level cache)",
+                 "achieved": round(rope_cold_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(rope_cold_gbs / PEAK_HBM_GBS, 4),
+                 "launch_ms_mean": round(rope_cold_mean, 5), "host_us_per_call": round(rope_host_us, 1),
+                 "achieved_mall_warm": round(rope_gbs, 1),
+                 "frac_mall_warm": round(rope_gbs / PEAK_HBM_GBS, 4),
+                 "launch_ms_mean_mall_warm": round(rope_mean, 5),
+                 "q_and_k_as_two_launches_gbs_mall_warm":
+                     round(rope_bytes / ((rope_q_mean + rope_k_mean) * 1e-3) / 1e9, 1)},
         "cpu_baseline": None,
     }
     ring.close()
