@@ -799,10 +799,14 @@ __global__ __launch_bounds__(512, 1) void chunk_attn8_kernel(const AttnParams p)
     return xhalf_max(fmaxf(m0, m1));
   };
   const int nk_local = nk - t_begin * kKT;
-  // Mask keys past the end of the range (only in the last tile), then decide
-  // the lazy rescale for the sub-tile whose exponentials come next.  O is
-  // rescaled here, after the previous sub-tile's P*V (formed against the old
-  // max) was issued; the hardware orders the accumulator update after it.
+  // Lazy rescale.  The decision for sub-tile j is taken on its row max
+  // before its exponentials: the running max and sum move at once.  O is
+  // rescaled one sub-step later, once P(j-1) -- formed against the old max
+  // and accumulated during sub-step j -- is in it (o_pending carries the
+  // factor).  Keys past the end of the range (only in the last tile) are
+  // masked first.
+  float o_alpha = 1.f;
+  bool o_pending = false;  // wave-uniform
   auto prepare = [&](int j, f32x16& S, float mx) __attribute__((always_inline)) {
     const int nvalid = nk_local - j * 32;
     if (nvalid < 32) {
@@ -816,43 +820,72 @@ __global__ __launch_bounds__(512, 1) void chunk_attn8_kernel(const AttnParams p)
     const bool need = mx * sl2 > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float m_new = fmaxf(m_run, mx * sl2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      o_alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
-      l_run *= alpha;
+      l_run *= o_alpha;
+      o_pending = true;
+    }
+  };
+  auto rescale_o = [&]() __attribute__((always_inline)) {
+    if (o_pending) {
       asm volatile("; rescale O" ::: "memory");
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
+      for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      }
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= o_alpha;
+      o_pending = false;
     }
   };
 
-  constexpr int NQK = C::NDC;       // QK slots
-  constexpr int NPV = 2 * C::NDB;   // PV slots (one per V fragment)
+  constexpr int NQK = C::NDC;       // QK MFMAs per sub-step
+  constexpr int NPV = 2 * C::NDB;   // PV MFMAs per sub-step (one per V fragment)
+  static_assert(NQK == NPV, "QK and PV slots pair up");
+  constexpr int NS = NQK + NPV;     // MFMA slots per sub-step
+  constexpr int RA = NS / 2;        // fragment reads run RA slots ahead of their MFMA
   constexpr int NE = 8;             // exponential units (2 keys each) per sub-tile
-  constexpr int E_PER = (NE + NQK - 1) / NQK;
-  constexpr int K_PER = (C::NDC + NPV - 1) / NPV;  // K fragment reads per PV slot
-  constexpr int MX0 = NPV >= 8 ? 2 : 1;            // first PV slot of the row max
-  constexpr int MX_UNITS = 4;                      // 4 values each
-  constexpr int MX_PER = (MX_UNITS + (NPV - MX0) - 1) / (NPV - MX0);
+  static_assert(NS % NE == 0, "exponential units spread evenly");
+  constexpr int DMA_EVERY = (NS + RA) / NDMA;  // DMA issues spread over the slots after the barrier
+  // Slot order of a sub-step: Q0 P0 Q1 P1 ... Q(n-3) P(n-3) Q(n-2) Q(n-1)
+  // P(n-2) P(n-1) (Q = a QK MFMA, P = a PV MFMA): the last QK comes two slots
+  // before the end, so S(j+1) is done when its row max is taken.
+  constexpr auto slot_is_q = [](int i) { return i < 2 * (NQK - 2) ? i % 2 == 0 : i < 2 * (NQK - 2) + 2; };
+  constexpr auto slot_idx = [](int i) {
+    return i < 2 * (NQK - 2) ? i / 2 : (i < 2 * (NQK - 2) + 2 ? NQK - 2 + (i - 2 * (NQK - 2)) : NPV - 2 + (i - 2 * (NQK - 2) - 2));
+  };
 
-  // One sub-step j: Sc = S(j) (already masked and max-checked), Sn receives
-  // S(j+1); vt/vkb: V of sub-tile j; kt2/kb2: K of sub-tile j+2; mid(): the
-  // tile barrier and DMA issue between the halves (or nothing).  Returns the
-  // row max of S(j+1).
-  auto substep = [&](const f32x16& Sc, f32x16& Sn, const lds_u8* vt, int vkb, const lds_u8* kt2,
-                     int kb2, auto&& mid, auto&& slot_hook) __attribute__((always_inline)) {
-    bf16x8 vfr[NPV];
-    uint32_t pk[8];
-    const float mneg = -m_run;
-    auto read_v = [&](int f) __attribute__((always_inline)) {  // f = half * NDB + db
-      const int half = f / C::NDB, db = f % C::NDB;
-      const lds_u8* a = vt + v_off + db * 4 * kColPitch + (vkb * 32 + half * 16) * 16;
+  // Operand fragments in flight: a ring of RA registers; the fragment of
+  // slot i lives in fr[i % RA], read from LDS RA slots before slot i, into
+  // the register the MFMA of slot i - RA has just read.
+  bf16x8 fr[RA];
+  struct Src {
+    const lds_u8* t;
+    int kb;
+  };
+  auto read_frag = [&](int slot, Src k, Src v) __attribute__((always_inline)) {
+    const int idx = slot_idx(slot);
+    if (slot_is_q(slot)) {
+      fr[slot % RA] = *(const lds_bf16x8*)(k.t + k_off + 2 * idx * kColPitch + k.kb * 512);
+    } else {
+      const int half = idx / C::NDB, db = idx % C::NDB;
+      const lds_u8* a = v.t + v_off + db * 4 * kColPitch + (v.kb * 32 + half * 16) * 16;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
       const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * 16));
-      vfr[f] = __builtin_bit_cast(bf16x8, (s16x8){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
-    };
+      fr[slot % RA] = __builtin_bit_cast(bf16x8, (s16x8){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+    }
+  };
+
+  // One sub-step j.  On entry: Sc = S(j) (masked, max checked), Pp = P(j-1),
+  // the ring holds the fragments of slots 0 .. RA-1.  The matrix cores
+  // alternate S(j+1) = K(j+1) Q^T and O^T += V(j-1)^T P(j-1)^T; slot i also
+  // reads the fragment of slot i+RA -- from K(j+1) / V(j-1) (cur) while that
+  // is in this sub-step, else from K(j+2) / V(j) (nxt).  The vector ALUs form
+  // P(j) = exp2(S(j) * scale - m) into Pn across the slots; mid() runs after
+  // slot RA-1 (the tile barrier, when there is one), hook(i) after slot i.
+  // Returns the row max of S(j+1).
+  auto substep = [&](const f32x16& Sc, f32x16& Sn, const bf16x8 (&Pp)[2], bf16x8 (&Pn)[2], Src curK,
+                     Src curV, Src nxtK, Src nxtV, auto&& mid, auto&& hook) __attribute__((always_inline)) {
+    uint32_t pk[8];
+    const float mneg = -m_run;
     auto exp_unit = [&](int e) __attribute__((always_inline)) {
       float s0 = Sc[2 * e], s1 = Sc[2 * e + 1];
       asm volatile("" : "+v"(s0), "+v"(s1));
@@ -864,85 +897,86 @@ __global__ __launch_bounds__(512, 1) void chunk_attn8_kernel(const AttnParams p)
       asm volatile("" ::"v"(pk[e]), "v"(l_run));
     };
 #pragma unroll
-    for (int i = 0; i < NQK; ++i) {
-      Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qreg[i], i == 0 ? (f32x16){} : Sn, 0, 0, 0);
-#pragma unroll
-      for (int f = i * NPV / NQK; f < (i + 1) * NPV / NQK; ++f) read_v(f);
-#pragma unroll
-      for (int k = 0; k < E_PER; ++k)
-        if (i * E_PER + k < NE) exp_unit(i * E_PER + k);
-      slot_hook(i);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const bf16x8 P0 = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    const bf16x8 P1 = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
-    mid();
-    __builtin_amdgcn_sched_barrier(0);
-    float mq[MX_UNITS];
-    float mx = 0.f;
-#pragma unroll
-    for (int m = 0; m < NPV; ++m) {
-      const int half = m / C::NDB, db = m % C::NDB;
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[m], half ? P1 : P0, oacc[db], 0, 0, 0);
-#pragma unroll
-      for (int k = 0; k < K_PER; ++k)
-        if (m * K_PER + k < C::NDC) read_k(kt2, kb2, m * K_PER + k);
-#pragma unroll
-      for (int k = 0; k < MX_PER; ++k) {
-        const int t = (m - MX0) * MX_PER + k;
-        if (m >= MX0 && t < MX_UNITS) {
-          mq[t] = fmaxf(fmaxf(Sn[4 * t], Sn[4 * t + 1]), fmaxf(Sn[4 * t + 2], Sn[4 * t + 3]));
-          asm volatile("" ::"v"(mq[t]));
-          if (t == MX_UNITS - 1) {
-            mx = xhalf_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
-            asm volatile("" ::"v"(mx));
-          }
-        }
+    for (int i = 0; i < NS; ++i) {
+      const int idx = slot_idx(i);
+      if (slot_is_q(i)) {
+        Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % RA], qreg[idx], idx == 0 ? (f32x16){} : Sn, 0, 0, 0);
+      } else {
+        oacc[idx % C::NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % RA], Pp[idx / C::NDB],
+                                                                      oacc[idx % C::NDB], 0, 0, 0);
       }
+      if (i + RA < NS)
+        read_frag(i + RA, curK, curV);
+      else
+        read_frag(i + RA - NS, nxtK, nxtV);
+      if (i % (NS / NE) == NS / NE - 1) exp_unit(i / (NS / NE));
+      if (i == RA - 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        mid();
+      }
+      hook(i);
       __builtin_amdgcn_sched_barrier(0);
     }
-    return mx;
+    Pn[0] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    Pn[1] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
+    rescale_o();  // after P(j-1) V(j-1) was issued, before P(j) V(j)
+    return rowmax16(Sn);
   };
 
-  // ---- prologue: tiles 0 .. NBUF-2 in flight; S(0) and its row max --------
+  // ---- prologue -------------------------------------------------------------
+  // Tiles 0 .. NBUF-2 in flight; buffer NBUF-1 stands for "tile -1" in the
+  // first sub-step (V(-1), multiplied by P(-1) = 0) and is zeroed so that the
+  // product is exactly 0.  Then S(0), its row max, the first ring fill.
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u) {
     tile_rows(u);
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) dma_col(c, KB[u], VB[u]);
   }
+  for (int o = tid * 16; o < C::TILE_BYTES; o += C::THREADS * 16)
+    *(lds_bf16x8*)(VB[NBUF - 1] + o) = (bf16x8){};
   wait_vmcnt<(NBUF - 2) * NDMA>();
   tile_barrier<(NBUF - 2) * NDMA>();
   f32x16 SA, SB;
+  bf16x8 PA[2], PB[2];
+  {
+    bf16x8 k0[C::NDC];
 #pragma unroll
-  for (int dc = 0; dc < C::NDC; ++dc) read_k(KB[0], 0, dc);
+    for (int dc = 0; dc < C::NDC; ++dc) k0[dc] = *(const lds_bf16x8*)(KB[0] + k_off + 2 * dc * kColPitch);
 #pragma unroll
-  for (int dc = 0; dc < C::NDC; ++dc) {
-    SA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dc], qreg[dc], dc == 0 ? (f32x16){} : SA, 0, 0, 0);
+    for (int dc = 0; dc < C::NDC; ++dc)
+      SA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0[dc], qreg[dc], dc == 0 ? (f32x16){} : SA, 0, 0, 0);
   }
 #pragma unroll
-  for (int dc = 0; dc < C::NDC; ++dc) read_k(KB[0], 1, dc);
+  for (int i = 0; i < RA; ++i) read_frag(i, Src{KB[0], 1}, Src{VB[NBUF - 1], 1});
+  PB[0] = PB[1] = (bf16x8){};
   prepare(0, SA, rowmax16(SA));
 
-  // Sub-steps 2u and 2u+1 of local tile u (buffer u % NBUF).  The barrier in
-  // the middle of sub-step 2u: this wave's DMA of tile u+1 has landed, every
-  // wave is done with tile u-1.  After it the DMA of tile u+NBUF-1, into the
-  // buffer tile u-1 left, is issued one column per QK slot across sub-step
-  // 2u+1 (only the DMA of tile u+NBUF-2 may then be in flight at the next
-  // barrier when NBUF = 4; NBUF = 3 waits for everything).
+  // Sub-steps 2u and 2u+1 of local tile u (buffer u % NBUF).  The barrier
+  // after slot RA-1 of sub-step 2u: this wave's DMA of tile u+1 has landed
+  // (its K is first read right after), every wave has read the last of
+  // tile u-1 (V(2u-1), read up to slot RA-1 of sub-step 2u).  After it the
+  // DMA of tile u+NBUF-1, into the buffer tile u-1 left, is issued one column
+  // at a time over the remaining slots of the tile (only the DMA of tile
+  // u+NBUF-2 may then be in flight at the next barrier when NBUF = 4; NBUF =
+  // 3 waits for everything).
   auto tile_steps = [&](int u, auto ph_) __attribute__((always_inline)) {
     constexpr int ph = decltype(ph_)::value;
     constexpr int nx = (ph + 1) % NBUF;
-    constexpr int fr = (ph + NBUF - 1) % NBUF;
-    float mx = substep(SA, SB, VB[ph], 0, KB[nx], 0, [&]() __attribute__((always_inline)) {
-      tile_barrier<(NBUF - 3) * NDMA>();
-      tile_rows(u + NBUF - 1);
-    }, [](int) {});
+    constexpr int pv = (ph + NBUF - 1) % NBUF;  // tile u-1, freed at the barrier
+    auto dma = [&](int pos) __attribute__((always_inline)) {  // pos: slots since the barrier
+      if (pos >= 0 && pos % DMA_EVERY == DMA_EVERY / 2 && pos / DMA_EVERY < NDMA)
+        dma_col(pos / DMA_EVERY, KB[pv], VB[pv]);
+    };
+    float mx = substep(SA, SB, PB, PA, Src{KB[ph], 1}, Src{VB[pv], 1}, Src{KB[nx], 0}, Src{VB[ph], 0},
+                       [&]() __attribute__((always_inline)) {
+                         tile_barrier<(NBUF - 3) * NDMA>();
+                         tile_rows(u + NBUF - 1);
+                       },
+                       [&](int i) __attribute__((always_inline)) { dma(i - RA); });
     prepare(2 * u + 1, SB, mx);
-    mx = substep(SB, SA, VB[ph], 1, KB[nx], 1, []() {}, [&](int i) __attribute__((always_inline)) {
-      constexpr int every = NQK / NDMA;
-      if (i % every == every - 1) dma_col(i / every, KB[fr], VB[fr]);
-    });
+    mx = substep(SB, SA, PA, PB, Src{KB[nx], 0}, Src{VB[ph], 0}, Src{KB[nx], 1}, Src{VB[ph], 1},
+                 []() {}, [&](int i) __attribute__((always_inline)) { dma(NS - RA + i); });
     prepare(2 * u + 2, SA, mx);
   };
   int u = 0;
@@ -952,10 +986,27 @@ __global__ __launch_bounds__(512, 1) void chunk_attn8_kernel(const AttnParams p)
     tile_steps(u + 2, std::integral_constant<int, 2>{});
     if constexpr (NBUF == 4) tile_steps(u + 3, std::integral_constant<int, 3>{});
   }
+  // The remaining tiles, each with its phase (u % NBUF).
   if (u < n_local) tile_steps(u++, std::integral_constant<int, 0>{});
   if (u < n_local) tile_steps(u++, std::integral_constant<int, 1>{});
   if constexpr (NBUF == 4)
     if (u < n_local) tile_steps(u++, std::integral_constant<int, 2>{});
+  // P(2n-1) V(2n-1): the last sub-tile's P*V (PB holds P(2n-1); V(2n-1) is
+  // the second half of the last tile, in buffer (n_local-1) % NBUF).
+  {
+    const int lb = (n_local - 1) % NBUF;
+    const lds_u8* vl = lb == 0 ? VB[0] : lb == 1 ? VB[1] : lb == 2 ? VB[2] : VB[3];
+#pragma unroll
+    for (int m = 0; m < NPV; ++m) {
+      const int half = m / C::NDB, db = m % C::NDB;
+      const lds_u8* a = vl + v_off + db * 4 * kColPitch + (32 + half * 16) * 16;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
+      const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * 16));
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, (s16x8){lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, PB[half], oacc[db], 0, 0, 0);
+    }
+  }
+  rescale_o();
   // No DMA may still be writing this workgroup's LDS when it retires.
   wait_vmcnt<0>();
 
