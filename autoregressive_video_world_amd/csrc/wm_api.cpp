@@ -107,7 +107,9 @@ struct Layout {
   size_t layer_bytes;
   size_t tab_off;
   size_t hw;        // byte offset of the (cos, sin) table of the h then w band
-  size_t tab_bytes, total;
+  size_t tab_bytes;
+  size_t cnt_off, cnt_bytes;  // split-attention arrival counters (int32, zeroed at creation)
+  size_t total;
 };
 
 wm_status check_desc(const wm_kvring_desc* d, Bands* bands) {
@@ -152,6 +154,18 @@ wm_status check_desc(const wm_kvring_desc* d, Bands* bands) {
   return WM_OK;
 }
 
+// Attention wave tasks: 32 queries of one q head each, eight per workgroup
+// (256 queries of one kv head's group).
+constexpr int kWaveQ = 32;
+constexpr int kWgWaves = 8;
+
+int task_blocks_of(int64_t nq) { return (int)((nq + kWaveQ - 1) / kWaveQ); }
+
+int wg_per_bg_of(const wm_kvring_desc& d, int64_t nq) {
+  const int group = d.n_q_heads / d.n_kv_heads;
+  return (group * task_blocks_of(nq) + kWgWaves - 1) / kWgWaves;
+}
+
 Layout layout_of(const wm_kvring_desc& d, const Bands& b) {
   Layout L;
   const size_t ft = (size_t)ft_of(d);
@@ -165,7 +179,12 @@ Layout layout_of(const wm_kvring_desc& d, const Bands& b) {
   L.hw = L.tab_off;
   // At least one entry: the kernels read entry 0 (unused) for t-band pairs.
   L.tab_bytes = (entries ? entries : 1) * 2 * sizeof(double);
-  L.total = align_up(L.tab_off + L.tab_bytes, 256);
+  // One counter per row block of the largest attention launch group.
+  const size_t groups = (size_t)std::min(d.batch, wm::kAttnMaxB) * d.n_kv_heads *
+                        wg_per_bg_of(d, (int64_t)d.max_chunk * ft_of(d));
+  L.cnt_off = align_up(L.tab_off + L.tab_bytes, 256);
+  L.cnt_bytes = align_up(groups * sizeof(int32_t), 256);
+  L.total = L.cnt_off + L.cnt_bytes;
   return L;
 }
 
@@ -296,7 +315,7 @@ wm_status finish(hipStream_t s) {
 // A planned launch: its spec and the parameter struct it takes.
 struct PLaunch {
   wm::LaunchSpec spec;
-  bool attn;             // parameters: ap (attention / combine) or rp (RoPE / append)
+  bool attn;             // parameters: ap (attention) or rp (RoPE / append)
   wm::RopeParams rp;
   wm::AttnParams ap;
   void* argv[1];
@@ -484,7 +503,7 @@ wm_status do_append(wm_kvring* r, const wm_bf16* k_raw, const wm_bf16* v, int n_
 // in ceil(n_wg / CUs) rounds; splitting every key range s ways multiplies the
 // workgroups by s and divides their length by s, so time goes as
 // ceil(n_wg * s / CUs) / s.  Each split adds a partial row per query and head
-// (d fp32 written, then read by the combine: ~8d bytes at ~5 TB/s) against
+// (d fp32 written, then read by the merge: ~8d bytes at ~5 TB/s) against
 // 4*Nk*d flop of attention per row at ~1 PFLOP/s, i.e. ~400/Nk of the
 // attention time per split.  Each split keeps at least two 64-key tiles.
 constexpr int kCUs = 256;
@@ -504,7 +523,7 @@ int choose_split(int n_wg, int ntiles) {
   if (forced) return std::max(1, std::min(forced, ntiles));
   const double per_split = 400.0 / (64.0 * ntiles);
   int best = 1;
-  double best_cost = std::ceil((double)n_wg / kCUs);  // unsplit: whole rounds, no combine
+  double best_cost = std::ceil((double)n_wg / kCUs);  // unsplit: whole rounds, no merge
   for (int s = 2; s <= kMaxSplit && ntiles >= 2 * s; ++s) {
     const double rounds = std::ceil((double)n_wg * s / kCUs);
     const double cost = rounds / s + per_split * s;
@@ -516,36 +535,18 @@ int choose_split(int n_wg, int ntiles) {
   return best;
 }
 
+// Rows of split partials: every 32-query task block whole (the kernel keeps
+// them in its lanes' register order, padding rows included).
+size_t split_rows(int nsplit, int nb, int nq, int hq) {
+  return (size_t)nsplit * nb * hq * task_blocks_of(nq) * kWaveQ;
+}
+
 size_t split_ws_bytes(int nsplit, int nb, int nq, int hq, int hd) {
-  const size_t rows = (size_t)nsplit * nb * nq * hq;
+  const size_t rows = split_rows(nsplit, nb, nq, hq);
   return align_up(rows * hd * sizeof(float), 256) + rows * 2 * sizeof(float);
 }
 
-// Attention wave tasks: 32-query blocks per wave.  1 = eight waves per
-// workgroup, two per SIMD, 32 queries each; 2 = four waves, one per SIMD,
-// 64 queries each.  Either way a workgroup covers 256 queries of one kv head.
-// WM_ATTN_FORM=4 selects the four-wave form and WM_ATTN_BUFS=3 three LDS tile
-// buffers (instead of four) in the eight-wave form (measurement).
-int wave_qblocks() {
-  const char* e = getenv("WM_ATTN_FORM");
-  return (e && atoi(e) == 4) ? 2 : 1;
-}
-
-int tile_bufs() {
-  const char* e = getenv("WM_ATTN_BUFS");
-  return (e && atoi(e) == 3) ? 3 : 4;
-}
-
-int task_blocks_of(const wm_kvring* r, int n_frames) {
-  const int q_per_task = 32 * wave_qblocks();
-  return (n_frames * r->ft + q_per_task - 1) / q_per_task;
-}
-
-int wg_per_bg_of(const wm_kvring* r, int n_frames) {
-  const int group = r->desc.n_q_heads / r->desc.n_kv_heads;
-  const int waves = 8 / wave_qblocks();
-  return (group * task_blocks_of(r, n_frames) + waves - 1) / waves;
-}
+int wg_per_bg_of(const wm_kvring* r, int n_frames) { return wg_per_bg_of(r->desc, (int64_t)n_frames * r->ft); }
 
 // The attention launch groups of a call: up to kAttnMaxB active rollouts each,
 // in batch order, with the split each would take given unlimited workspace.
@@ -606,9 +607,8 @@ wm_status do_attn(const wm_kvring* r, int layer, const wm_bf16* q, const wm_bf16
   p.ft = r->ft;
   p.nq = n_frames * r->ft;
   p.ring_slots = r->R;
-  p.wave_qblocks = wave_qblocks();
-  p.tile_bufs = tile_bufs();
-  p.nqb = task_blocks_of(r, n_frames);
+  p.nqb = task_blocks_of(p.nq);
+  p.counters = reinterpret_cast<int32_t*>(r->pool + r->L.cnt_off);
   p.wg_per_bg = wg_per_bg_of(r, n_frames);
   const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)d.head_dim));
   p.scale_log2e = (float)((double)sc * 1.4426950408889634);
@@ -624,7 +624,7 @@ wm_status do_attn(const wm_kvring* r, int layer, const wm_bf16* q, const wm_bf16
     p.part_o = nullptr;
     p.part_ml = nullptr;
     if (ns > 1) {
-      const size_t rows = (size_t)ns * p.nb * p.nq * p.hq;
+      const size_t rows = split_rows(ns, p.nb, p.nq, p.hq);
       p.part_o = static_cast<float*>(ws);
       p.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                            align_up(rows * d.head_dim * sizeof(float), 256));
@@ -855,6 +855,7 @@ wm_status wm_kvring_create(const wm_kvring_desc* desc, void* dev_pool, size_t po
     fill(desc->frame_h, bands.dh);
     fill(desc->frame_w, bands.dw);
     hipError_t e = hipMemcpy(r->pool + L.tab_off, host.data(), L.tab_bytes, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemset(r->pool + L.cnt_off, 0, L.cnt_bytes);
     if (e != hipSuccess) {
       delete r;
       return hip_fail(e, "table upload");

@@ -89,13 +89,12 @@ struct AttnParams {
   uint16_t* out;          // [B][Nq][Hq][d]
   float* part_o;          // split-KV partial outputs (nullptr: no split)
   float* part_ml;         // split-KV (max, sum) per row
+  int32_t* counters;      // split-KV arrival counters, one per row block (zero between launches)
   int32_t hq, hkv, group; // group = Hq / Hkv
   int32_t ft;             // tokens per frame
   int32_t nq;             // queries per rollout = n_frames * Ft
   int32_t ring_slots;     // R = S + W
-  int32_t wave_qblocks;   // 32-query blocks per wave task: 1 (8 waves) or 2 (4 waves)
-  int32_t tile_bufs;      // 8-wave form: 64-key LDS tile buffers (3 or 4)
-  int32_t nqb;            // wave-task query blocks (32 * wave_qblocks queries) per rollout
+  int32_t nqb;            // 32-query wave tasks per rollout and q head
   int32_t wg_per_bg;      // workgroups per (rollout, kv head) per split
   int32_t nsplit;         // key-range splits (1 = none)
   int32_t n_wg;           // logical workgroups (set by the launcher)
@@ -115,9 +114,9 @@ constexpr size_t kScratchBytes = (size_t)128 << 20;
 // the first call with the device current, then cached per device.
 hipError_t scratch_region(void** ptr);
 
-// Launches of one attention group: fills p's derived fields (workgroup count,
-// XCD stride) and returns the attention launch and, when the key range is
-// split, the combine launch (both take p); 0 if the shape is not built.
+// The launch of one attention group: fills p's derived fields (workgroup
+// count, XCD stride) and returns the number of launches (1; 0 if the shape
+// is not built).  A split launch merges its partials itself.
 int chunk_attn_specs(AttnParams& p, int head_dim, LaunchSpec specs[2]);
 
 }  // namespace wm

@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--extra-workloads", default="3,4,5,6",
                     help="comma-separated workload ids whose steady-state attention is also timed "
                          "(0 = none): drive, the 32/8-head GQA workload (key-range split and "
-                         "combine), eight drive rollouts in one call and the four-view workload "
+                         "merge), eight drive rollouts in one call and the four-view workload "
                          "by default")
     ap.add_argument("--modes-workload", type=int, default=1,
                     help="second workload whose rollout step is timed eager / finalize stream / graph "
@@ -91,11 +91,8 @@ def kernel_source_digest():
 
 
 def attn_kernel_name(head_dim):
-    """The attention kernel the library launches (the eight-wave form unless
-    WM_ATTN_FORM=4 selects the four-wave one)."""
-    if os.environ.get("WM_ATTN_FORM") == "4":
-        return "chunk_attn_kernel<%d, 2>" % head_dim
-    return "chunk_attn8_kernel<%d, %d>" % (head_dim, 3 if os.environ.get("WM_ATTN_BUFS") == "3" else 4)
+    """The attention kernel the library launches."""
+    return "chunk_attn_kernel<%d>" % head_dim
 
 
 def profiled_traffic(workload_name, key="traffic_bytes_per_launch"):
@@ -526,8 +523,8 @@ def main():
     torch.cuda.synchronize()
 
     # Steady-state attention of other workloads: the same kernel at other
-    # shapes, the key-range split and its combine where the grid is small
-    # (launch time = attention + combine), several camera views per frame.
+    # shapes, the key-range split and its merge where the grid is small (the
+    # merge runs inside the attention launch), several camera views per frame.
     extras = []
     for wid in [int(x) for x in args.extra_workloads.split(",") if x.strip()]:
         if wid in (0, args.workload):

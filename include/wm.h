@@ -159,6 +159,10 @@ typedef struct {
  *   tables : (cos, sin) pairs of the h and w RoPE bands, [frame_h][d_h/2]
  *            then [frame_w][d_w/2]: fp64 copies of fp32-rounded values,
  *            256-byte aligned
+ *   counters: int32, one per row block of the largest attention launch
+ *            (min(B, 64) * Hkv * ceil(Hq/Hkv * ceil(C*Ft/32) / 8)), rounded up
+ *            to 256 bytes: arrivals of the workgroups of a key-range split,
+ *            zero between calls (the last arrival resets its counter)
  * Slot of frame f of a sequence: f if f < S, else S + (f - S) mod W.
  */
 size_t wm_kvring_pool_bytes(const wm_kvring_desc* desc);
@@ -166,7 +170,8 @@ size_t wm_kvring_pool_bytes(const wm_kvring_desc* desc);
 /* Create a ring over a caller-owned device pool of at least
  * wm_kvring_pool_bytes(desc) bytes (16-byte aligned, valid until destroy).
  * Writes the RoPE h/w tables into the pool's table area with a synchronous
- * host-to-device copy; K/V slot contents are left as they are.  Every
+ * host-to-device copy and zeroes the counters; K/V slot contents are left
+ * as they are.  Every
  * rollout starts empty at t0 = 0.
  * dev_pool == NULL with pool_bytes == 0 creates a metadata-only ring: appends
  * update the bookkeeping and reports only (no device access), and

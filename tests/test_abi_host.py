@@ -46,13 +46,23 @@ def ring_for(wl, meta=True):
                      wl.n_sink, wl.window, wl.chunk, meta_only=meta, n_views=wl.n_views)
 
 
+def up256(x):
+    return (x + 255) // 256 * 256
+
+
 def test_pool_bytes_formula():
+    """K and V halves, the h/w tables, then one int32 arrival counter per row
+    block of the largest attention launch (min(B, 64) rollouts x Hkv kv heads
+    x workgroups of 256 queries of a kv head's group), each region 256-aligned."""
     for wl in WORKLOADS.values():
         r = ring_for(wl)
         half = wl.batch * (wl.n_sink + wl.window) * wl.n_kv_heads * wl.ft * wl.head_dim * 2
-        assert r.pool_bytes >= 2 * half
-        assert r.pool_bytes - 2 * half < 2 * 256 + 4 * 4 * (wl.frame_h + wl.frame_w) * wl.head_dim
-        assert r.pool_bytes % 256 == 0
+        dhw = 2 * (wl.head_dim // 6)
+        tables = (wl.frame_h + wl.frame_w) * (dhw // 2) * 16
+        group = wl.n_q_heads // wl.n_kv_heads
+        wg = -(-group * -(-wl.chunk * wl.ft // 32) // 8)
+        counters = min(wl.batch, 64) * wl.n_kv_heads * wg * 4
+        assert r.pool_bytes == 2 * up256(half) + up256(tables) + up256(counters), wl.name
         r.close()
 
 

@@ -84,7 +84,7 @@ def run_case(wl, t0s=None, use_step=False, q_scale=1.0, split=False):
     """Drive ``wl`` through the library and the oracle; compare everything.
 
     split=True hands the library a workspace, so launches with few
-    workgroups split their key ranges and combine partials."""
+    workgroups split their key ranges and merge partials."""
     with forced_split(3 if split else 0):
         return _run_case(wl, t0s, use_step, q_scale, split)
 
@@ -167,6 +167,15 @@ def _run_case(wl, t0s, use_step, q_scale, split):
             check_pool(ring, oracles, used)
     for b in range(B):
         assert ring.view(b)["retained"] == oracles[b].retained()
+    if split:
+        # the split launches' arrival counters (the pool's last region) are
+        # back at zero: the last workgroup of every row block reset its own
+        torch.cuda.synchronize()
+        group = wl.n_q_heads // wl.n_kv_heads
+        wg = -(-group * -(-wl.chunk * wl.ft // 32) // 8)
+        n_cnt = min(B, 64) * wl.n_kv_heads * wg
+        cnt = ring.pool[-((n_cnt * 4 + 255) // 256 * 256):].view(torch.int32)
+        assert int(cnt.abs().sum()) == 0, cnt.nonzero()
     ring.close()
     return worst
 
@@ -632,7 +641,7 @@ def test_full_size_steady_state_sampled(cfg):
 def test_two_runs_bit_identical(split, monkeypatch):
     """Determinism: the same rollout on two rings from the same seeded inputs
     gives bit-identical outputs at every denoise step and identical pool
-    bytes, the key-range split and its combine included."""
+    bytes, the key-range split and its merge included."""
     wl = W(160, batch=2, n_q_heads=8, n_kv_heads=2, frame_h=9, frame_w=11, chunk=2, window=3,
            n_gen=10, n_denoise=2)
     if split:
