@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=25)
-    ap.add_argument("--workload", type=int, default=2, help="workload id (1-5), default 2")
+    ap.add_argument("--workload", type=int, default=2, help="single-rollout workload id (1-4 or 6), default 2")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=12, help="q heads in the oracle sample")
