@@ -12,7 +12,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libwm.so")
+# WM_LIB names another build of the same library (e.g. a host-sanitized one).
+LIB_PATH = os.environ.get("WM_LIB") or os.path.join(_HERE, "libwm.so")
 
 WM_MAX_CHUNK = 16
 WM_MAX_RING = 256

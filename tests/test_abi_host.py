@@ -41,6 +41,17 @@ def test_exports_every_declared_symbol():
     assert set(decl) <= exported
 
 
+def test_loaded_library_is_the_named_build():
+    """The process maps the library WM_LIB names (the in-package one when
+    unset): the sanitizer runs rely on it."""
+    wm.lib()
+    want = os.path.realpath(os.environ.get("WM_LIB") or os.path.join(ROOT, "autoregressive_video_world_amd",
+                                                                     "libwm.so"))
+    maps = open("/proc/self/maps").read()
+    assert want in maps
+    assert os.path.realpath(binding.LIB_PATH) == want
+
+
 def ring_for(wl, meta=True):
     return wm.KVRing(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
                      wl.n_sink, wl.window, wl.chunk, meta_only=meta, n_views=wl.n_views)
