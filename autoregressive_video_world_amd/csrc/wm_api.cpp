@@ -218,6 +218,18 @@ struct wm_kvring {
   uint64_t serial = 0;  // distinguishes a ring from a later one at the same address
 };
 
+namespace {
+// One planned kernel launch: its shape and its parameter block.
+struct PLaunch {
+  wm::LaunchSpec spec;
+  bool attn;             // parameters: ap (attention) or rp (RoPE / append)
+  wm::RopeParams rp;
+  wm::AttnParams ap;
+  void* argv[1];
+  void* args() { return attn ? static_cast<void*>(&ap) : static_cast<void*>(&rp); }
+};
+}  // namespace
+
 struct wm_rollout_graph {
   wm_kvring* ring;
   uint64_t ring_serial;
@@ -235,6 +247,7 @@ struct wm_rollout_graph {
   bool launched = false;
   std::vector<hipGraphNode_t> nodes;
   std::vector<wm::LaunchSpec> shape;
+  std::vector<PLaunch> held;  // the parameters each node of the instance holds
 };
 
 namespace {
@@ -313,14 +326,6 @@ wm_status finish(hipStream_t s) {
 
 // --- where the workers' launches go ---------------------------------------
 // A planned launch: its spec and the parameter struct it takes.
-struct PLaunch {
-  wm::LaunchSpec spec;
-  bool attn;             // parameters: ap (attention) or rp (RoPE / append)
-  wm::RopeParams rp;
-  wm::AttnParams ap;
-  void* argv[1];
-  void* args() { return attn ? static_cast<void*>(&ap) : static_cast<void*>(&rp); }
-};
 
 // Kernel-node parameters of a planned launch (points into L: L must stay put
 // until the node is added or updated).
@@ -751,7 +756,13 @@ hipError_t build_graph(wm_rollout_graph* g, std::vector<PLaunch>& plan) {
     }
   }
   if (e == hipSuccess) e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+  if (e == hipSuccess) g->held = plan;
   return e;
+}
+
+bool same_params(PLaunch& a, PLaunch& b) {
+  return a.attn == b.attn &&
+         memcmp(a.args(), b.args(), a.attn ? sizeof(wm::AttnParams) : sizeof(wm::RopeParams)) == 0;
 }
 
 // Drops the graph and its instance once their last launch has finished.
@@ -765,6 +776,7 @@ void drop_graph(wm_rollout_graph* g) {
   g->graph = nullptr;
   g->nodes.clear();
   g->shape.clear();
+  g->held.clear();
 }
 
 // Arguments of wm_rope3d (for each tensor of wm_rope3d_pair).
@@ -1141,9 +1153,14 @@ wm_status wm_rollout_graph_launch(wm_rollout_graph* g, wm_append_report* rep, in
   if ((st = wait_finalize(ring, s)) != WM_OK) return st;
   hipError_t e = hipSuccess;
   if (same) {
+    // Only the nodes whose parameters changed since their last update (in
+    // steady state: the RoPE rows' positions and the append's slots; an
+    // attention over a full window keeps its parameters).
     for (size_t i = 0; e == hipSuccess && i < plan.size(); ++i) {
+      if (same_params(plan[i], g->held[i])) continue;
       hipKernelNodeParams kp = node_params(plan[i]);
       e = hipGraphExecKernelNodeSetParams(g->exec, g->nodes[i], &kp);
+      if (e == hipSuccess) g->held[i] = plan[i];
     }
   } else {
     // New launch shapes (the window filling, a different key split): a new
