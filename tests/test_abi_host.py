@@ -431,21 +431,26 @@ def test_refused_append_launch_keeps_bookkeeping(monkeypatch):
 def test_rings_in_parallel_host_threads():
     """Separate rings from separate host threads at once (ctypes releases the
     GIL during the calls): the handle registry stays consistent, each ring's
-    bookkeeping is its own, and each thread reads its own last error."""
+    bookkeeping is its own (every report equals the oracle deque's), and each
+    thread reads its own last error.  The sanitizer tests run this under
+    ThreadSanitizer."""
     import threading
     L = wm.lib()
     errors = []
+    start = threading.Barrier(8)
 
     def worker(tid):
         try:
+            start.wait()
             for it in range(150):
                 S, W = 1 + tid % 3, 2 + it % 4
                 r = wm.KVRing(2, 4, 2, 128, 3, 4, S, W, 2, meta_only=True)
+                dq = DequeRing(S, W)
                 n = 1 + (tid + it) % 9
                 for _ in range(n):
-                    r.append_evict(None, None, 1)
+                    assert r.append_evict(None, None, 1, active=[1, 0])[0] == oracle_append(dq, 1, 0)
                 v = r.view(0)
-                assert v["n_committed"] == n and len(v["retained"]) == min(n, S + W), (tid, it)
+                assert v["n_committed"] == n and v["retained"] == view_of(dq, 0), (tid, it)
                 # a failing call: this thread's message, not another's
                 bad = "rollout %d out of range" % (7 + tid)
                 assert L.wm_kvring_reset(r._h, 7 + tid, 0) == 1
@@ -460,3 +465,17 @@ def test_rings_in_parallel_host_threads():
     for t in threads:
         t.join()
     assert not errors, errors[:3]
+
+
+def test_handle_destroyed_in_another_thread_is_refused():
+    """The registry is shared: a handle destroyed by one thread is no longer
+    live for any other."""
+    import threading
+    r = wm.KVRing(1, 2, 2, 64, 2, 2, 1, 2, 1, meta_only=True)
+    h = r._h
+    t = threading.Thread(target=r.close)
+    t.start()
+    t.join()
+    L = wm.lib()
+    assert L.wm_kvring_reset(h, 0, 0) == 3   # WM_E_STATE
+    assert b"not live" in L.wm_last_error()

@@ -2,8 +2,8 @@
 
 A host-sanitized copy of libwm.so (device code unchanged, rebuilt here when
 a source or the build script is newer) is loaded through WM_LIB by a child
-pytest run of the host ABI tests and of the threaded host-call test, with the
-sanitizer's runtime preloaded.  Any sanitizer report fails the run
+pytest run of the host ABI tests (eight threads calling at once among them),
+with the sanitizer's runtime preloaded.  Any sanitizer report fails the run
 (halt_on_error), and the copy must really be instrumented: its undefined
 symbols include the sanitizer's hooks.  Under AddressSanitizer the
 interpreter allocates through malloc (PYTHONMALLOC=malloc), so the buffers
@@ -21,7 +21,7 @@ import pytest
 from autoregressive_video_world_amd import _build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-FILES = ["tests/test_abi_host.py", "tests/test_host_threads.py"]
+FILES = ["tests/test_abi_host.py"]
 HOOK = {"address": "__asan_report_load", "thread": "__tsan_read"}
 
 
