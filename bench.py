@@ -78,15 +78,17 @@ def _code_only(text):
 def kernel_source_digest():
     """sha256 over the code of the kernel sources and the internal header
     (comments and layout ignored: they do not change the compiled kernels)
-    and over the build script, which holds the compile flags."""
+    and over the product build's compile flags."""
     import hashlib
+    from autoregressive_video_world_amd import _build
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "autoregressive_video_world_amd", "csrc")
     for rel in ("kernels/chunk_attn.hip", "kernels/rope_append.hip", "wm_internal.hpp"):
         with open(os.path.join(csrc, rel)) as f:
             h.update(_code_only(f.read()).encode())
-    with open(os.path.join(ROOT, "autoregressive_video_world_amd", "_build.py"), "rb") as f:
-        h.update(f.read())
+    flags = {"common": [f for f in _build.COMMON if not f.startswith("-I")],
+             "per_file": {k.replace(os.sep, "/"): v for k, v in sorted(_build.PER_FILE.items())}}
+    h.update(json.dumps(flags, sort_keys=True).encode())
     return h.hexdigest()
 
 
@@ -402,6 +404,52 @@ def main():
     attn_each = per_launch(attn, args.kernel_reps)
     attn_p50 = attn_each[len(attn_each) // 2]
     attn_p90 = attn_each[min(len(attn_each) - 1, (9 * len(attn_each)) // 10)]
+    # Power context (a diagnostic beside the metric, not part of it): under
+    # this kernel the card runs at its board power limit, and the power of the
+    # matrix cores depends on the operand bits.  The same launch over a ring
+    # and chunk of all-zero K/V/Q, and a plain bf16 GEMM through torch (the
+    # vendor library) on N(0,1) and on all-zero operands, show how much of the
+    # gap to the quoted peak is the power limit on random data.
+    power_ctx = None
+    if not args.steady_only:
+        zring = wm.KVRing(1, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.frame_h, wl.frame_w,
+                          wl.n_sink, wl.window, wl.chunk, device=dev, n_views=wl.n_views)
+        zkv = torch.zeros(1, C * ft, wl.n_kv_heads, wl.head_dim, dtype=torch.bfloat16, device=dev)
+        filled = 0
+        while filled < wl.n_sink + wl.window:
+            n = min(C, wl.n_sink + wl.window - filled)
+            zring.append_evict(zkv[:, :n * ft], zkv[:, :n * ft], n)
+            filled += n
+        zq = torch.zeros_like(q_rot)
+        zout = torch.empty_like(q_rot)
+        zattn = lambda: zring.chunk_attn(zq, zkv, zkv, C, out=zout, workspace=ws)
+        zattn()
+        torch.cuda.synchronize()
+        z_mean, _ = timed(zattn, args.kernel_reps)
+        zring.close()
+        del zkv, zq, zout
+        n_g = 8192
+        gflop = 2.0 * n_g ** 3
+
+        def gemm_tflops(a, b):
+            c = torch.empty(n_g, n_g, dtype=torch.bfloat16, device=dev)
+            t, _ = timed(lambda: torch.matmul(a, b, out=c), 40)
+            return gflop / (t * 1e-3) / 1e12
+
+        ga, gb = randn(n_g, n_g), randn(n_g, n_g)
+        g_rand = gemm_tflops(ga, gb)
+        ga.zero_()
+        gb.zero_()
+        g_zero = gemm_tflops(ga, gb)
+        del ga, gb
+        power_ctx = {
+            "note": "diagnostic, not the metric: the board power limit and operand-dependent matrix-core power",
+            "attn_zero_inputs_tflops": round(wl.attn_flops() / (z_mean * 1e-3) / 1e12, 1),
+            "attn_zero_inputs_frac": round(wl.attn_flops() / (z_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "attn_zero_inputs_launch_ms_mean": round(z_mean, 4),
+            "gemm_bf16_%d_randn_tflops" % n_g: round(g_rand, 1),
+            "gemm_bf16_%d_zeros_tflops" % n_g: round(g_zero, 1),
+        }
     rope_mean, rope_host_us = timed(lambda: ring.rope3d_pair(qs[0], ks[0], C, y=q_rot, y2=k_rot),
                                     args.kernel_reps, busy)
     rope_q_mean, _ = timed(lambda: ring.rope3d(qs[0], C, y=q_rot), args.kernel_reps, busy)
@@ -623,6 +671,7 @@ def main():
                    "achieved_mall_warm": round(app_gbs, 1),
                    "frac_mall_warm": round(app_gbs / PEAK_HBM_GBS, 4),
                    "launch_ms_mean_mall_warm": round(app_mean, 5)},
+        "power_context": power_ctx,
         "append_size_sweep": sweep,
         "rollout_modes": ([modes] if modes else []) + ([modes_small] if modes_small else []),
         "append_layers": layers,
