@@ -58,7 +58,6 @@
 // the softmax never produces NaN from finite inputs; -inf is still honoured.
 #include "../wm_internal.hpp"
 
-#include <mutex>
 #include <type_traits>
 
 namespace wm {
@@ -592,35 +591,6 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_kernel(const AttnParams p) 
 }
 
 }  // namespace
-
-// ---------------------------------------------------------------------------
-// Scratch of the allocation-free entry point.  Host code never passes the
-// array's name to a kernel (on the host it is only a stand-in): it passes the
-// device address scratch_region() looked up for the current device.
-// ---------------------------------------------------------------------------
-static __device__ __align__(256) uint8_t scratch[kScratchBytes];
-
-namespace {
-constexpr int kMaxDevices = 64;
-std::mutex g_scratch_mutex;
-void* g_scratch[kMaxDevices];
-}  // namespace
-
-hipError_t scratch_region(void** ptr) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_scratch_mutex);
-  if (!g_scratch[dev]) {
-    void* p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (e != hipSuccess) return e;
-    g_scratch[dev] = p;
-  }
-  *ptr = g_scratch[dev];
-  return hipSuccess;
-}
 
 int chunk_attn_specs(AttnParams& p, int head_dim, LaunchSpec specs[2]) {
   if (head_dim != 128 && head_dim != 64) return 0;
