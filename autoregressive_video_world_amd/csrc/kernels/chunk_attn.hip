@@ -96,11 +96,17 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // Split partials are exchanged between workgroups that may run on different
 // XCDs, whose L2 caches are not coherent with each other.  They move with
 // 16-byte buffer loads and stores that carry the agent-scope coherence bit
-// (sc1): such accesses are coherent across the device without any L2
-// writeback or invalidation.  The descriptor covers one wave's block, so its
-// base must be wave-uniform (read from the first lane).
-// (m, l) pairs move as two 4-byte accesses: this compiler's 8-byte buffer
-// load builtin returns its first word in both halves.
+// (sc1), the encoding the compiler itself gives agent-scope atomic loads
+// and stores: such accesses are coherent across the device without any L2
+// writeback or invalidation.  Ordering: each wave waits for its stores to
+// complete (vmcnt 0) before the barrier that precedes the workgroup's
+// arrival atomic, and the merging workgroup issues its loads only after its
+// own atomic returned -- release and acquire for these accesses, without the
+// whole-L2 writeback and invalidation a fence over plain accesses costs.
+// A descriptor covers one wave's block, so its base must be wave-uniform
+// (taken from the first active lane).  (m, l) pairs move as two 4-byte
+// accesses: this compiler's 8-byte buffer-load builtin returns its first
+// word in both halves.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSc1 = 16;  // cache-policy operand bit for sc1
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* base, int bytes);
