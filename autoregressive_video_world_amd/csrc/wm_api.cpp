@@ -14,6 +14,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <set>
 #include <string>
@@ -504,15 +505,35 @@ wm_status do_append(wm_kvring* r, const wm_bf16* k_raw, const wm_bf16* v, int n_
   return WM_OK;
 }
 
-// Key-range split of an attention launch.  A launch of n_wg workgroups runs
-// in ceil(n_wg / CUs) rounds; splitting every key range s ways multiplies the
-// workgroups by s and divides their length by s, so time goes as
-// ceil(n_wg * s / CUs) / s.  Each split adds a partial row per query and head
-// (d fp32 written, then read by the merge: ~8d bytes at ~5 TB/s) against
-// 4*Nk*d flop of attention per row at ~1 PFLOP/s, i.e. ~400/Nk of the
-// attention time per split.  Each split keeps at least two 64-key tiles.
+// Key-range split of an attention launch.  Launch time of s splits, in
+// times of one workgroup's 64-key tile, a model fitted to launches with every
+// forced count (1-6, 8) on four workloads (152 to 880 workgroups, 275 to 1100
+// key tiles; it picks the fastest count on each):
+//  - the n_wg * s workgroups run in rounds of one per CU; a round lasts the
+//    tiles each walks, ceil(ntiles / s), plus a fixed kWgFixedTiles per
+//    workgroup (Q load, pipeline fill and drain, partial write);
+//  - a partly filled round is shorter, as the clock rises when fewer CUs
+//    draw power (the card runs this kernel at its power limit): its time
+//    scales by max(kRoundFloor, f^kRoundExp) at busy fraction f;
+//  - the partials (written, then read by the merge) add kMergeTiles per 256
+//    workgroups of the launch.
+// Each split keeps at least two 64-key tiles.
 constexpr int kCUs = 256;
 constexpr int kMaxSplit = wm::kAttnMaxSplit;
+constexpr double kWgFixedTiles = 4.0;
+constexpr double kMergeTiles = 4.0;
+constexpr double kRoundExp = 0.6;
+constexpr double kRoundFloor = 0.7;
+
+double split_cost(int n_wg, int ntiles, int s) {
+  const int64_t n = (int64_t)n_wg * s;
+  const int64_t full = n / kCUs, rem = n % kCUs;
+  const double rounds =
+      (double)full + (rem ? std::max(kRoundFloor, std::pow((double)rem / kCUs, kRoundExp)) : 0.0);
+  double cost = rounds * ((double)((ntiles + s - 1) / s) + kWgFixedTiles);
+  if (s > 1) cost += kMergeTiles * (double)n / kCUs;
+  return cost;
+}
 
 // WM_ATTN_SPLIT=n (1..8) overrides the choice (tuning and tests); read on
 // every call.
@@ -526,12 +547,10 @@ int forced_split() {
 int choose_split(int n_wg, int ntiles) {
   const int forced = forced_split();
   if (forced) return std::max(1, std::min(forced, ntiles));
-  const double per_split = 400.0 / (64.0 * ntiles);
   int best = 1;
-  double best_cost = std::ceil((double)n_wg / kCUs);  // unsplit: whole rounds, no merge
+  double best_cost = split_cost(n_wg, ntiles, 1);
   for (int s = 2; s <= kMaxSplit && ntiles >= 2 * s; ++s) {
-    const double rounds = std::ceil((double)n_wg * s / kCUs);
-    const double cost = rounds / s + per_split * s;
+    const double cost = split_cost(n_wg, ntiles, s);
     if (cost < best_cost - 1e-9) {
       best = s;
       best_cost = cost;
