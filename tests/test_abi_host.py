@@ -479,3 +479,35 @@ def test_handle_destroyed_in_another_thread_is_refused():
     L = wm.lib()
     assert L.wm_kvring_reset(h, 0, 0) == 3   # WM_E_STATE
     assert b"not live" in L.wm_last_error()
+
+
+def split_rows_bytes(nsplit, hq, nq, d):
+    """Workspace of an nsplit-way key split: fp32 partials of every 32-query
+    task block whole (O/l, 256-aligned) and an (m, l) pair per row."""
+    rows = nsplit * hq * (-(-nq // 32)) * 32
+    return (rows * d * 4 + 255) // 256 * 256 + rows * 8
+
+
+def test_split_choice_of_the_workloads():
+    """The split count the launch-time model picks at each workload's steady
+    state (seen through the workspace it asks for), the fastest of every
+    forced count measured on the GPU: drive and sf13b unsplit, mot15 three
+    ways, the four-view workload two ways; small grids split up to 8 ways."""
+    want = {"sf13b": 0, "drive": 0, "mot15": 3, "drv4v": 2}
+    for wl in WORKLOADS.values():
+        if wl.name not in want:
+            continue
+        r = ring_for(wl)
+        for _ in range(wl.n_sink + wl.window):
+            r.append_evict(None, None, 1)
+        nq = wl.chunk * wl.ft
+        ns = want[wl.name]
+        assert r.workspace_bytes(wl.chunk) == (split_rows_bytes(ns, wl.n_q_heads, nq, wl.head_dim) if ns else 0), \
+            wl.name
+        r.close()
+    # one workgroup (2 q heads, 80 queries) over 33 key tiles: 7 ways
+    r = wm.KVRing(1, 2, 1, 64, 8, 10, 1, 24, 1, meta_only=True)
+    for _ in range(30):
+        r.append_evict(None, None, 1)
+    assert r.workspace_bytes(1) == split_rows_bytes(7, 2, 80, 64)
+    r.close()
