@@ -43,6 +43,9 @@
 //    per slot, while the vector ALUs form P(j); every operand fragment is
 //    read from LDS eight slots before its MFMA into a ring of eight
 //    registers;
+//  * while a wave forms its exponentials it takes issue priority over the
+//    other wave of its SIMD (s_setprio), so that its softmax, the longer
+//    dependent chain, is not starved by the other wave's MFMA slots;
 //  * online softmax in the log2 domain with a lazy rescale: the running max
 //    only moves (and O, l are rescaled) when a row's new max exceeds it by
 //    more than 8 (P stays <= 2^8); a wave-uniform branch, rarely taken;
@@ -417,7 +420,13 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_kernel(const AttnParams p) 
         read_frag(i + RA, curK, curV);
       else
         read_frag(i + RA - NS, nxtK, nxtV);
-      if (i % (NS / NE) == NS / NE - 1) exp_unit(i / (NS / NE));
+      // While a wave forms its exponentials (its longest-latency vector
+      // work) it has issue priority over the other wave of its SIMD.
+      if (i % (NS / NE) == NS / NE - 1) {
+        __builtin_amdgcn_s_setprio(1);
+        exp_unit(i / (NS / NE));
+        __builtin_amdgcn_s_setprio(0);
+      }
       if (i == RA - 1) {
         __builtin_amdgcn_sched_barrier(0);
         mid();
